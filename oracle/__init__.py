@@ -1,0 +1,165 @@
+"""Plain CPU oracle of the W1.58A8 BitLinear forward (ctypes wrapper over
+``bitlinear_oracle.c``).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` import this package. The product library never uses it.
+
+Every function takes and returns numpy arrays; the arithmetic is in the C file,
+whose header lists the passages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bitlinear_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/liboracle.so``."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        i64, f32, f64, vp = ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+        L.ora_abs_sum.argtypes = [vp, i64]
+        L.ora_abs_sum.restype = f64
+        L.ora_weight_scale.argtypes = [vp, i64]
+        L.ora_weight_scale.restype = f32
+        L.ora_weight_codes.argtypes = [vp, i64, f32, vp]
+        L.ora_weight_codes.restype = None
+        L.ora_pack.argtypes = [vp, i64, i64, vp]
+        L.ora_pack.restype = None
+        L.ora_unpack.argtypes = [vp, i64, i64, vp]
+        L.ora_unpack.restype = i64
+        L.ora_quantize_act.argtypes = [vp, i64, i64, vp, vp]
+        L.ora_quantize_act.restype = None
+        L.ora_quantize_act_norm.argtypes = [vp, i64, i64, vp, f32, ctypes.c_int, vp, vp, vp]
+        L.ora_quantize_act_norm.restype = None
+        L.ora_forward.argtypes = [vp, vp, i64, i64, vp, f32, i64, vp, vp]
+        L.ora_forward.restype = i64
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def abs_sum(w: np.ndarray) -> float:
+    """Pairwise binary64 sum of |w| over the flattened array (see O1 in the C file)."""
+    w = _c(w, np.float32).reshape(-1)
+    return float(lib().ora_abs_sum(_ptr(w), w.size))
+
+
+def weight_scale(w: np.ndarray) -> np.float32:
+    """gamma = max(fl32(pairwise_sum|W| / numel), 1e-8)."""
+    w = _c(w, np.float32).reshape(-1)
+    return np.float32(lib().ora_weight_scale(_ptr(w), w.size))
+
+
+def weight_codes(w: np.ndarray, gamma) -> np.ndarray:
+    w = _c(w, np.float32)
+    q = np.empty(w.shape, dtype=np.int8)
+    lib().ora_weight_codes(_ptr(w), w.size, np.float32(gamma), _ptr(q))
+    return q
+
+
+def pack(q: np.ndarray) -> np.ndarray:
+    q = _c(q, np.int8)
+    n, k = q.shape
+    if k % 4:
+        raise ValueError("K must be a multiple of 4")
+    out = np.empty((n, k // 4), dtype=np.uint8)
+    lib().ora_pack(_ptr(q), n, k, _ptr(out))
+    return out
+
+
+def unpack(packed: np.ndarray, k: int):
+    """Returns (codes [N][K] int8, number of unused 0b11 fields seen)."""
+    packed = _c(packed, np.uint8)
+    n = packed.shape[0]
+    q = np.empty((n, k), dtype=np.int8)
+    bad = lib().ora_unpack(_ptr(packed), n, k, _ptr(q))
+    return q, int(bad)
+
+
+def pack_weights(w: np.ndarray):
+    """Latent fp32 W [N][K] -> (packed uint8 [N][K/4], gamma fp32, codes int8 [N][K])."""
+    gamma = weight_scale(w)
+    q = weight_codes(w, gamma)
+    return pack(q), gamma, q
+
+
+def quantize_act(x: np.ndarray):
+    """x fp32 [M][K] -> (xq int8 [M][K], s fp32 [M])."""
+    x = _c(x, np.float32)
+    m, k = x.shape
+    xq = np.empty((m, k), dtype=np.int8)
+    s = np.empty(m, dtype=np.float32)
+    lib().ora_quantize_act(_ptr(x), m, k, _ptr(xq), _ptr(s))
+    return xq, s
+
+
+def quantize_act_norm(u: np.ndarray, gain, eps: float, relu2: bool):
+    """Fused [ReLU^2] -> RMSNorm(gain, eps) -> absmax quant; gain None = no norm."""
+    u = _c(u, np.float32)
+    m, k = u.shape
+    xq = np.empty((m, k), dtype=np.int8)
+    s = np.empty(m, dtype=np.float32)
+    work = np.empty(k, dtype=np.float32)
+    g = None if gain is None else _c(gain, np.float32)
+    lib().ora_quantize_act_norm(_ptr(u), m, k, None if g is None else _ptr(g), np.float32(eps),
+                                1 if relu2 else 0, _ptr(xq), _ptr(s), _ptr(work))
+    return xq, s
+
+
+def forward(xq: np.ndarray, s: np.ndarray, q: np.ndarray, gamma):
+    """xq [M][K] int8, s [M], q [N][K] int8 codes, gamma -> (acc int32 [M][N], y fp32 [M][N])."""
+    xq = _c(xq, np.int8)
+    s = _c(s, np.float32)
+    q = _c(q, np.int8)
+    m, k = xq.shape
+    n, k2 = q.shape
+    if k != k2:
+        raise ValueError("K mismatch")
+    acc = np.empty((m, n), dtype=np.int32)
+    y = np.empty((m, n), dtype=np.float32)
+    ovf = lib().ora_forward(_ptr(xq), _ptr(s), m, k, _ptr(q), np.float32(gamma), n, _ptr(acc), _ptr(y))
+    if ovf:
+        raise OverflowError("%d accumulators exceed int32" % ovf)
+    return acc, y
+
+
+def bitlinear(x: np.ndarray, w: np.ndarray, gain=None, eps: float = 1e-5, relu2: bool = False):
+    """Whole path on latent inputs: quantize W and x, accumulate, rescale."""
+    packed, gamma, q = pack_weights(w)
+    if gain is None and not relu2:
+        xq, s = quantize_act(x)
+    else:
+        xq, s = quantize_act_norm(x, gain, eps, relu2)
+    acc, y = forward(xq, s, q, gamma)
+    return dict(packed=packed, gamma=gamma, q=q, xq=xq, s=s, acc=acc, y=y)

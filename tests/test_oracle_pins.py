@@ -1,0 +1,316 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-derived examples (tests/golden/hand_examples.json), closed forms, library
+routines (math.fsum, numpy integer matmul, scipy special functions), brute force in
+fp64, and invariants of the definitions. Each test names the mistake it would catch.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import gammainc, gammaln, ndtr
+
+import datagen
+
+F32 = np.float32
+
+
+# ----------------------------------------------------------------------------- O1 gamma
+
+def test_gamma_gaussian_closed_form(ora):
+    """E|W| = sigma*sqrt(2/pi) for W ~ N(0, sigma^2). Catches a dropped abs, a wrong
+    divisor (N instead of N*K) or a per-row mean."""
+    w = datagen.gaussian_weights(2560, 2560, datagen.stream_id(1, role=1))
+    g = float(ora.weight_scale(w))
+    expect = 0.02 * math.sqrt(2.0 / math.pi)
+    se = expect * math.sqrt(math.pi / 2.0 - 1.0) / math.sqrt(w.size)
+    assert abs(g - expect) < 5 * se, (g, expect, se)
+
+
+def test_abs_sum_vs_fsum_bound(ora):
+    """Pairwise binary64 sum against the correctly rounded sum (math.fsum) within the
+    pairwise error bound ceil(log2 n) * 2^-53 * sum|x|."""
+    rng = datagen.rng(99)
+    for n in (1, 2, 3, 7, 1000, 65537, 1 << 20):
+        w = (rng.standard_normal(n) * rng.uniform(0.01, 100.0)).astype(np.float32)
+        s = ora.abs_sum(w)
+        exact = math.fsum(abs(float(v)) for v in w)
+        bound = max(1, math.ceil(math.log2(max(n, 2)))) * 2.0 ** -53 * exact
+        assert abs(s - exact) <= bound, (n, s, exact)
+
+
+def test_abs_sum_is_pairwise_not_sequential(ora):
+    """[1, 0, 0, 0, 2^-53, 2^-53] (n = 6, tree padded to 8): the pairwise tree adds the
+    two 2^-53 first, giving 1 + 2^-52 exactly; a left-to-right sum loses both (1.0)."""
+    t = 2.0 ** -53
+    w = np.array([1.0, 0.0, 0.0, 0.0, t, t], dtype=np.float32)
+    assert ora.abs_sum(w) == 1.0 + 2.0 ** -52
+    seq = 0.0
+    for v in w:
+        seq += abs(float(v))
+    assert seq == 1.0
+
+
+def test_gamma_floor_and_sign_pattern(ora):
+    """All-zero W takes the 1e-8 floor; W = c * sign pattern gives gamma = c and q = sign."""
+    z = np.zeros((4, 8), dtype=np.float32)
+    assert ora.weight_scale(z) == F32(1e-8)
+    packed, gamma, q = ora.pack_weights(z)
+    assert (q == 0).all()
+    signs = np.where(datagen.rng(5).random((16, 64)) < 0.5, -1.0, 1.0).astype(np.float32)
+    w = signs * F32(0.0123)
+    packed, gamma, q = ora.pack_weights(w)
+    assert gamma == F32(0.0123)
+    assert (q == signs.astype(np.int8)).all()
+
+
+# ----------------------------------------------------------------------------- O2 codes
+
+def test_weight_ties_golden(ora, golden):
+    """Hand example: ties go to even and codes are clipped to [-1, 1]."""
+    g = golden["weight_ties"]
+    w = np.array(g["W"], dtype=np.float32)
+    packed, gamma, q = ora.pack_weights(w)
+    assert gamma == F32(g["gamma"])
+    assert q.tolist() == g["codes"]
+    assert packed.tolist() == g["packed"]
+
+
+def test_codes_brute_force_tiny(ora):
+    """Codes against a direct restatement on python floats (fp32 quotient through numpy
+    scalars, round-half-even through Python's round) on a tiny matrix."""
+    w = datagen.gaussian_weights(7, 12, 77)
+    gamma = ora.weight_scale(w)
+    q = ora.weight_codes(w, gamma)
+    for i in range(7):
+        for k in range(12):
+            r = round(float(F32(w[i, k]) / F32(gamma)))
+            assert q[i, k] == max(-1, min(1, r))
+
+
+def test_gaussian_split_closed_form(ora):
+    """For Gaussian latents P(q=0) = 2*Phi(sqrt(2/pi)/2) - 1 = 0.31006. Catches the
+    threshold-at-mean variant (57.5% zeros) and a half-away rounding of the ratio."""
+    w = datagen.gaussian_weights(2048, 2048, datagen.stream_id(1, role=2))
+    _, gamma, q = ora.pack_weights(w)
+    p0 = float((q == 0).mean())
+    expect = 2.0 * ndtr(math.sqrt(2.0 / math.pi) / 2.0) - 1.0
+    assert abs(p0 - expect) < 2e-3, (p0, expect)
+    assert abs(float((q == 1).mean()) - (1 - expect) / 2) < 2e-3
+    threshold_variant = 2.0 * ndtr(math.sqrt(2.0 / math.pi)) - 1.0
+    assert abs(p0 - threshold_variant) > 0.2
+
+
+def test_trained_like_split_matches_pages(ora):
+    """Generalized-Gaussian (beta = 0.846) latents: closed form through the regularized
+    incomplete gamma, and the pages' trained-weight split 42% / 29% / 29%
+    (BitNet b1.58 深度解析 s.2.3) within half a percent."""
+    b = datagen.GG_BETA_TRAINED
+    w = datagen.gg_weights(1024, 4096, datagen.stream_id(2, role=3))
+    _, gamma, q = ora.pack_weights(w)
+    p0 = float((q == 0).mean())
+    pp = float((q == 1).mean())
+    pm = float((q == -1).mean())
+    t = math.exp(gammaln(2 / b) - gammaln(1 / b)) / 2
+    expect0 = gammainc(1 / b, t ** b)
+    assert abs(p0 - expect0) < 2e-3
+    assert abs(p0 - 0.42) < 0.005 and abs(pp - 0.29) < 0.005 and abs(pm - 0.29) < 0.005
+
+
+# ----------------------------------------------------------------------------- O3 pack
+
+def test_pack_golden_and_roundtrip(ora, golden):
+    g = golden["pack_order"]
+    q = np.array(g["codes"], dtype=np.int8)
+    p = ora.pack(q)
+    assert p.tolist() == g["packed"]
+    w = datagen.gaussian_weights(33, 260, 3)
+    packed, gamma, q = ora.pack_weights(w)
+    q2, bad = ora.unpack(packed, 260)
+    assert bad == 0 and (q2 == q).all()
+    fields = np.stack([(packed >> (2 * i)) & 3 for i in range(4)])
+    assert (fields != 3).all()
+
+
+def test_pack_rejects_ragged_k(ora):
+    with pytest.raises(ValueError):
+        ora.pack(np.zeros((2, 6), dtype=np.int8))
+
+
+# ----------------------------------------------------------------------------- O4 act quant
+
+def test_act_quant_golden(ora, golden):
+    g = golden["act_quant"]
+    xq, s = ora.quantize_act(np.array(g["X"], dtype=np.float32))
+    assert s.tolist() == g["scale"]
+    assert xq.tolist() == g["codes"]
+
+
+def test_act_quant_invariants(ora):
+    """Per-token max|xq| = 127 exactly; odd symmetry; power-of-two scale invariance;
+    tokens with different ranges get different scales (per token, not per tensor)."""
+    x = datagen.outlier_acts(64, 2560, 11)
+    x[3] *= 1000.0
+    xq, s = ora.quantize_act(x)
+    assert (np.abs(xq.astype(np.int32)).max(axis=1) == 127).all()
+    assert (xq != -128).all()
+    assert s[3] < s[2] / 100.0
+    xq2, s2 = ora.quantize_act(-x)
+    assert (xq2 == -xq).all() and (s2 == s).all()
+    xq3, s3 = ora.quantize_act(x * F32(8.0))
+    assert (xq3 == xq).all() and (s3 == s / F32(8.0)).all()
+
+
+def test_act_quant_brute_force(ora):
+    """Every code against a restatement with numpy fp32 scalars and round-half-even."""
+    x = datagen.outlier_acts(3, 300, 12)
+    xq, s = ora.quantize_act(x)
+    for t in range(3):
+        m = max(float(np.abs(x[t]).max()), 1e-8)
+        st = F32(127.0) / F32(m)
+        assert s[t] == st
+        for k in range(300):
+            r = round(float(F32(x[t, k]) * st))
+            assert xq[t, k] == max(-128, min(127, r))
+
+
+def test_act_quant_zero_row(ora):
+    x = np.zeros((2, 8), dtype=np.float32)
+    xq, s = ora.quantize_act(x)
+    assert (xq == 0).all() and s[0] == F32(127.0) / F32(1e-8)
+
+
+# ----------------------------------------------------------------------------- O5 prologue
+
+def test_prologue_golden(ora, golden):
+    g = golden["relu2_norm"]
+    u = np.array(g["U"], dtype=np.float32)
+    xq, s = ora.quantize_act_norm(u, np.array(g["gain"], np.float32), g["eps"], True)
+    assert xq.tolist() == g["codes"]
+    expect = F32(31.75 * math.sqrt(4.015625 + float(F32(g["eps"]))))
+    assert s[0] == expect
+
+
+def test_prologue_constant_row_closed_form(ora):
+    """u_k = a, g = 1: RMSNorm output is a/sqrt(a^2+eps) for every k, so codes are
+    127*sign(a) and the stored scale is (127/|a|) * sqrt(a^2 + eps)."""
+    for a in (2.0, -0.75, 1e-3):
+        u = np.full((1, 256), a, dtype=np.float32)
+        xq, s = ora.quantize_act_norm(u, np.ones(256, np.float32), 1e-5, False)
+        assert (xq == (127 if a > 0 else -127)).all()
+        ref = (127.0 / abs(a)) * math.sqrt(a * a + float(F32(1e-5)))
+        assert abs(float(s[0]) - ref) <= 2 * abs(ref) * 2.0 ** -24
+
+
+def test_prologue_matches_normalize_then_quantize(ora):
+    """Independent check of the reading that the norm's per-token factor cancels:
+    normalize in fp64 (v/sqrt(mean v^2 + eps) * g), quantize in fp64, and compare.
+    Codes may differ only where x*s lands within rounding noise of a .5 boundary
+    (at most by 1, very rarely); scales agree to a few fp32 ulps."""
+    u = datagen.outlier_acts(32, 6912, 21)
+    g = datagen.gains(6912, 22)
+    for relu2 in (False, True):
+        xq, s = ora.quantize_act_norm(u, g, 1e-5, relu2)
+        v = u.astype(np.float64)
+        if relu2:
+            v = np.maximum(v, 0.0) ** 2
+        r = 1.0 / np.sqrt((v * v).mean(axis=1, keepdims=True) + float(F32(1e-5)))
+        xn = v * r * g.astype(np.float64)
+        sn = 127.0 / np.abs(xn).max(axis=1, keepdims=True)
+        ref = np.clip(np.round(xn * sn), -128, 127).astype(np.int32)
+        diff = np.abs(ref - xq.astype(np.int32))
+        assert diff.max() <= 1
+        assert (diff > 0).mean() < 1e-4
+        assert np.allclose(s.astype(np.float64), sn[:, 0], rtol=3e-7, atol=0)
+
+
+def test_prologue_codes_equal_plain_quant_of_gained_input(ora):
+    """The codes of the fused path are the plain absmax codes of fl(v * g) and do not
+    depend on eps or on a power-of-two scaling of u (without ReLU^2)."""
+    u = datagen.outlier_acts(8, 2560, 31)
+    g = datagen.gains(2560, 32)
+    xq, s = ora.quantize_act_norm(u, g, 1e-5, False)
+    xq_plain, _ = ora.quantize_act((u * g).astype(np.float32))
+    assert (xq == xq_plain).all()
+    xq2, s2 = ora.quantize_act_norm(u * F32(4.0), g, 1e-5, False)
+    assert (xq2 == xq).all()
+    xq3, _ = ora.quantize_act_norm(u, g, 0.5, False)
+    assert (xq3 == xq).all()
+    ur = datagen.outlier_acts(8, 2560, 33)
+    xq4, _ = ora.quantize_act_norm(ur, g, 1e-5, True)
+    pos = np.maximum(ur, 0)
+    xq5, _ = ora.quantize_act((pos * pos * g).astype(np.float32))
+    assert (xq4 == xq5).all()
+    assert (xq4[ur <= 0] == 0).all()
+
+
+def test_prologue_without_gain_is_plain(ora):
+    u = datagen.outlier_acts(4, 512, 41)
+    xq, s = ora.quantize_act_norm(u, None, 1e-5, False)
+    xq2, s2 = ora.quantize_act(u)
+    assert (xq == xq2).all() and (s == s2).all()
+
+
+# ----------------------------------------------------------------------------- O6/O7 forward
+
+def test_forward_golden(ora, golden):
+    g = golden["forward"]
+    r = ora.bitlinear(np.array(g["X"], np.float32), np.array(g["W"], np.float32))
+    assert r["acc"].tolist() == g["acc"]
+    c = F32(1.0) / F32(127.0)
+    assert r["y"][0, 0] == F32(32.0) * c and r["y"][0, 1] == F32(-191.0) * c
+
+
+def test_forward_acc_vs_integer_matmul(ora):
+    """Accumulators against numpy's int64 matmul (a library primitive), non-square and
+    ragged shapes so that a transposed operand cannot pass."""
+    for (m, n, k) in ((1, 37, 260), (5, 64, 68), (3, 19, 1024)):
+        w = datagen.gg_weights(n, k, 100 + k)
+        x = datagen.outlier_acts(m, k, 200 + k)
+        r = ora.bitlinear(x, w)
+        ref = r["xq"].astype(np.int64) @ r["q"].astype(np.int64).T
+        assert (r["acc"].astype(np.int64) == ref).all()
+
+
+def test_forward_vs_dense_fp64_dequantized(ora):
+    """y against a dense fp64 product of the dequantized operands, (q*gamma) and
+    (xq/s): relative error within 3e-7 (two fp32 roundings) and exact zeros."""
+    m, n, k = 4, 96, 2560
+    w = datagen.gg_weights(n, k, 301)
+    x = datagen.outlier_acts(m, k, 302)
+    r = ora.bitlinear(x, w)
+    wd = r["q"].astype(np.float64) * float(r["gamma"])
+    xd = r["xq"].astype(np.float64) / r["s"].astype(np.float64)[:, None]
+    ref = xd @ wd.T
+    y = r["y"].astype(np.float64)
+    # fp64 round-off of the dense sum, used only where the exact result is zero
+    noise = 1e-13 * (np.abs(xd) @ np.abs(wd).T)
+    zero = np.abs(ref) <= noise
+    assert (y[zero] == 0).all()
+    rel = np.abs(y[~zero] - ref[~zero]) / np.abs(ref[~zero])
+    assert rel.max() < 3e-7
+    # and the quantized product approximates the latent product
+    latent = x.astype(np.float64) @ w.astype(np.float64).T
+    cos = (latent * ref).sum() / np.sqrt((latent ** 2).sum() * (ref ** 2).sum())
+    assert cos > 0.6
+
+
+def test_forward_one_hot(ora):
+    """A single nonzero activation x_k: xq = +-127 at k and y_n = gamma * q_nk * x_k
+    (the textbook special case) within a few ulp."""
+    n, k = 32, 64
+    w = datagen.gaussian_weights(n, k, 401)
+    x = np.zeros((1, k), dtype=np.float32)
+    x[0, 17] = F32(-3.25)
+    r = ora.bitlinear(x, w)
+    assert r["xq"][0, 17] == -127 and (np.delete(r["xq"][0], 17) == 0).all()
+    expect = float(r["gamma"]) * r["q"][:, 17].astype(np.float64) * -3.25
+    assert np.allclose(r["y"][0].astype(np.float64), expect, rtol=4e-7, atol=0)
+
+
+def test_forward_bound(ora):
+    """|acc| <= 127 * nnz(row of q)."""
+    w = datagen.gg_weights(64, 512, 501)
+    x = datagen.heavy_channel_acts(8, 512, 502)
+    r = ora.bitlinear(x, w)
+    nnz = (r["q"] != 0).sum(axis=1)
+    assert (np.abs(r["acc"]) <= 127 * nnz[None, :]).all()
