@@ -1,0 +1,136 @@
+/*
+ * bitlinear.h -- C ABI of the W1.58A8 BitLinear forward for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the BitNet b1.58 linear layer, a drop-in for nn.Linear without
+ * bias: y = x W^T with W of shape [out_features = N][in_features = K]
+ * ("BitNet b1.58 深度解析", s.2.2; "微软AI大模型炸场", s.2 "架构基础与创新" and
+ * "偏置移除"). Weights are absmean-quantized to ternary codes {-1, 0, +1} and stored
+ * four per byte; activations are quantized per token to int8 with absmax scaling;
+ * the product is accumulated exactly in int32 and rescaled to fp32.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a HIP device pointer to caller-owned, row-major,
+ *     contiguous memory, unless stated otherwise. Float and int8 activation buffers
+ *     must be 16-byte aligned; outputs must not overlap any input.
+ *   - The library allocates no memory, keeps no pointer after it returns and has no
+ *     mutable global state; calls from several host threads are safe.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream). Arguments
+ *     are checked before any HIP call: on an error status nothing was enqueued.
+ *     A launch failure returns BITLINEAR_ERR_HIP (from hipGetLastError right after
+ *     the launch). A fault inside a kernel surfaces at the caller's next
+ *     synchronization with the stream.
+ *   - Sizes: 1 <= M, 1 <= N <= 2^31 - 1, 4 <= K <= BITLINEAR_MAX_K, K % 4 == 0,
+ *     M*K and N*K below 2^40. Non-finite inputs give unspecified results.
+ *   - Rounding: every fp32 quotient is an IEEE division and every code is rounded
+ *     half to even, so a CPU implementation of the same definitions reproduces the
+ *     quantized codes, packed bytes and int32 accumulators bit for bit.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITLINEAR_MAX_K (1 << 20)
+
+typedef enum {
+    BITLINEAR_OK = 0,
+    BITLINEAR_ERR_NULL = 1,      /* a required pointer is NULL */
+    BITLINEAR_ERR_SHAPE = 2,     /* a size is out of range or K % 4 != 0 */
+    BITLINEAR_ERR_ALIGN = 3,     /* a pointer lacks the alignment stated here */
+    BITLINEAR_ERR_WORKSPACE = 4, /* workspace smaller than bitlinear_pack_workspace_bytes */
+    BITLINEAR_ERR_ALIAS = 5,     /* an output buffer overlaps an input buffer */
+    BITLINEAR_ERR_HIP = 6        /* the HIP runtime rejected a launch */
+} bitlinear_status;
+
+/* Human-readable name of a status code; never NULL. */
+const char* bitlinear_status_string(int status);
+
+/*
+ * Weight quantization and packing (offline, once per matrix).
+ *
+ * gamma = mean |W| over the whole matrix ("absmean": "微软AI大模型炸场" s.1,
+ * "20亿参数仅0.4GB" s.2; one scale per tensor as in "BitNet b1.58 深度解析" s.2.2),
+ * summed in binary64 as a pairwise tree over the row-major array zero-padded to a
+ * power of two, divided by N*K in binary64, rounded to fp32 and floored at 1e-8.
+ * Code q = clip(round_half_even(W / gamma), -1, 1) with an fp32 division
+ * ("BitNet b1.58 深度解析" s.2.2: sign(w) round(|w|/alpha)).
+ * Packing ("微软AI大模型炸场" s.3: several ternary values in one 8-bit integer in HBM;
+ * "BitNet b1.58 深度解析" s.2.1: 2-bit codes, one of the four states unused):
+ * W_packed is uint8 [N][K/4]; byte j of row n holds codes k = 4j..4j+3, code 4j+i in
+ * bits 2i..2i+1 as the field value q + 1 (0 = -1, 1 = 0, 2 = +1; 3 never written).
+ *
+ *   W          fp32 [N][K], 16-byte aligned (read only)
+ *   W_packed   uint8 [N][K/4] (written)
+ *   gamma      fp32 [1] on the device (written; read by bitlinear_forward*)
+ *   workspace  device scratch of at least bitlinear_pack_workspace_bytes(N, K) bytes,
+ *              8-byte aligned; its contents are undefined afterwards. Two calls that
+ *              run concurrently need distinct workspaces.
+ */
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
+int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* W_packed, float* gamma,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Per-token absmax int8 activation quantization, with an optional fused subln input.
+ *
+ * Plain (gain == NULL, relu2 == 0): for token t, m = max_k |x_tk|,
+ * s_t = 127 / max(m, 1e-8) (fp32 division), xq_tk = clip(round_half_even(x_tk s_t),
+ * -128, 127) ("BitNet b1.58 深度解析" s.2.2; per token: "微软AI大模型炸场" s.1,
+ * "20亿参数仅0.4GB" s.2).
+ *
+ * Fused subln input (squared ReLU: "微软AI大模型炸场" s.2 "特殊设计"; subln RMSNorm:
+ * same page s.1, RMSNorm layers in "BitNet b1.58 深度解析" s.2.4):
+ *   v = relu2 ? max(u,0)^2 : u   (fp32);   w = v * gain (fp32) when gain != NULL.
+ * The RMSNorm output r*w, r = 1/sqrt(mean(v^2) + eps), differs from w by a positive
+ * per-token factor, which absmax quantization divides out; the codes are therefore
+ * those of w, with s' = 127 / max(max|w|, 1e-8), and the stored scale is that of the
+ * normalized activation, s_t = s' * sqrt(mean(v^2) + eps) (binary64, rounded to fp32).
+ * relu2 != 0 with gain == NULL applies only the squared ReLU.
+ *
+ *   X        fp32 [M][K], 16-byte aligned
+ *   gain     fp32 [K] or NULL (no RMSNorm); eps is used only when gain != NULL
+ *   Xq       int8 [M][K] (written), 4-byte aligned
+ *   x_scale  fp32 [M] (written): s_t, the multiplier; dequantization is xq / s_t
+ */
+int bitlinear_quantize_act(const float* X, int64_t M, int64_t K, const float* gain, float eps,
+                           int relu2, int8_t* Xq, float* x_scale, hipStream_t stream);
+
+/*
+ * The W1.58A8 product ("20亿参数仅0.4GB" s.2 BitLinear; custom W1.58A8 matmul kernel in
+ * "微软以小搏大 … 原生 1bit LLM", section "微软在 1 bit LLM 上的探索"; rescale
+ * y = (W_q x_q) * scale in "BitNet b1.58 深度解析" s.2.3):
+ *   acc[t][n] = sum_k q[n][k] * xq[t][k]           (exact, int32)
+ *   y[t][n]   = fl32(fl32(acc[t][n]) * fl32(gamma / s_t))
+ *
+ *   Xq        int8 [M][K], 4-byte aligned;   x_scale  fp32 [M]
+ *   W_packed  uint8 [N][K/4] as written by bitlinear_pack_weights, 16-byte aligned
+ *   gamma     fp32 [1] on the device
+ *   Y         fp32 [M][N] (written)
+ *   acc       int32 [M][N] (written) or NULL
+ * A packed field equal to 3 (never written by the packer) gives unspecified results.
+ */
+int bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K,
+                      const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int32_t* acc,
+                      hipStream_t stream);
+
+/*
+ * Fused input quantization and product in one launch: bit for bit the result of
+ * bitlinear_quantize_act(X, M, K, gain, eps, relu2, ...) followed by bitlinear_forward,
+ * without the int8 round trip through memory. Arguments as in those two calls.
+ */
+int bitlinear_forward_f32(const float* X, int64_t M, int64_t K, const float* gain, float eps, int relu2,
+                          const uint8_t* W_packed, const float* gamma, int64_t N, float* Y,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

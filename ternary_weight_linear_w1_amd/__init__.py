@@ -1,0 +1,176 @@
+"""W1.58A8 BitLinear forward on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/bitlinear.h`` (``libbitlinear.so``,
+built in-tree by ``ternary_weight_linear_w1_amd._build``). Every function here only
+checks and marshals arguments; all arithmetic runs in the HIP kernels. PyTorch is used
+for device memory and the current stream.
+
+The library must be built; importing works without a GPU, and every call that would
+launch work needs a ROCm device. There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ._build import LIB as _LIB_PATH
+
+__all__ = [
+    "BitLinearError", "lib", "status_string", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
+    "bitlinear_quantize_act", "bitlinear_forward", "bitlinear_forward_f32", "EXPORTED",
+]
+
+EXPORTED = (
+    "bitlinear_status_string",
+    "bitlinear_pack_workspace_bytes",
+    "bitlinear_pack_weights",
+    "bitlinear_quantize_act",
+    "bitlinear_forward",
+    "bitlinear_forward_f32",
+)
+
+_lib = None
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libbitlinear.so``; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libbitlinear.so is not built; run ternary_weight_linear_w1_amd._build.build()")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i64, f32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+        L.bitlinear_status_string.argtypes = [ci]
+        L.bitlinear_status_string.restype = ctypes.c_char_p
+        L.bitlinear_pack_workspace_bytes.argtypes = [i64, i64]
+        L.bitlinear_pack_workspace_bytes.restype = ctypes.c_size_t
+        L.bitlinear_pack_weights.argtypes = [vp, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
+        L.bitlinear_pack_weights.restype = ci
+        L.bitlinear_quantize_act.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, vp]
+        L.bitlinear_quantize_act.restype = ci
+        L.bitlinear_forward.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp]
+        L.bitlinear_forward.restype = ci
+        L.bitlinear_forward_f32.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, i64, vp, vp]
+        L.bitlinear_forward_f32.restype = ci
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().bitlinear_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise BitLinearError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions" % (name, ndim))
+
+
+def bitlinear_pack_workspace_bytes(N: int, K: int) -> int:
+    return int(lib().bitlinear_pack_workspace_bytes(int(N), int(K)))
+
+
+def bitlinear_pack_weights(W, packed=None, gamma=None, workspace=None, stream=None):
+    """Latent fp32 weights [N][K] -> (packed uint8 [N][K/4], gamma fp32 [1])."""
+    import torch
+    _need(W, torch.float32, "W", 2)
+    N, K = W.shape
+    if packed is None:
+        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    if gamma is None:
+        gamma = torch.empty((1,), dtype=torch.float32, device=W.device)
+    nbytes = bitlinear_pack_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 8),), dtype=torch.uint8, device=W.device)
+    _check(lib().bitlinear_pack_weights(_ptr(W), N, K, _ptr(packed), _ptr(gamma), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)),
+           "bitlinear_pack_weights")
+    return packed, gamma
+
+
+def bitlinear_quantize_act(X, gain=None, eps: float = 1e-5, relu2: bool = False, xq=None, scale=None,
+                           stream=None):
+    """fp32 activations [M][K] -> (int8 codes [M][K], per-token scale fp32 [M])."""
+    import torch
+    _need(X, torch.float32, "X", 2)
+    M, K = X.shape
+    if gain is not None:
+        _need(gain, torch.float32, "gain", 1)
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _check(lib().bitlinear_quantize_act(_ptr(X), M, K, _ptr(gain), float(eps), 1 if relu2 else 0, _ptr(xq),
+                                        _ptr(scale), _stream(stream)), "bitlinear_quantize_act")
+    return xq, scale
+
+
+def bitlinear_forward(Xq, x_scale, W_packed, gamma, y=None, acc=None, stream=None):
+    """int8 activations + packed ternary weights -> fp32 y [M][N] (and int32 acc if given)."""
+    import torch
+    _need(Xq, torch.int8, "Xq", 2)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    _need(W_packed, torch.uint8, "W_packed", 2)
+    _need(gamma, torch.float32, "gamma", 1)
+    M, K = Xq.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must have K/4 columns")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    if acc is True:
+        acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    _check(lib().bitlinear_forward(_ptr(Xq), _ptr(x_scale), M, K, _ptr(W_packed), _ptr(gamma), N, _ptr(y),
+                                   _ptr(acc if acc is not None and acc is not False else None), _stream(stream)),
+           "bitlinear_forward")
+    return (y, acc) if isinstance(acc, torch.Tensor) else y
+
+
+def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, relu2: bool = False, y=None,
+                          stream=None):
+    """Fused quantize + product from fp32 activations [M][K] -> fp32 y [M][N]."""
+    import torch
+    _need(X, torch.float32, "X", 2)
+    _need(W_packed, torch.uint8, "W_packed", 2)
+    _need(gamma, torch.float32, "gamma", 1)
+    if gain is not None:
+        _need(gain, torch.float32, "gain", 1)
+    M, K = X.shape
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must have K/4 columns")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    _check(lib().bitlinear_forward_f32(_ptr(X), M, K, _ptr(gain), float(eps), 1 if relu2 else 0, _ptr(W_packed),
+                                       _ptr(gamma), N, _ptr(y), _stream(stream)), "bitlinear_forward_f32")
+    return y

@@ -1,0 +1,309 @@
+// bitlinear_api.hip -- C ABI of the W1.58A8 BitLinear library (declared in
+// include/bitlinear.h): argument checks, kernel choice and launches on the caller's
+// stream. Nothing here allocates memory or keeps state besides a per-device cache of
+// the compute-unit count.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stdint.h>
+
+#include "../../include/bitlinear.h"
+#include "device_common.hpp"
+#include "gemv.hpp"
+#include "pack.hpp"
+#include "quant.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 256;
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+            c = 256;
+        g_cu_count[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
+bool aligned(const void* p, uintptr_t a)
+{
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes)
+{
+    if (!a || !b)
+        return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int check_mk(int64_t M, int64_t K)
+{
+    if (M < 1 || K < 4 || K > BITLINEAR_MAX_K || (K % 4) != 0)
+        return BITLINEAR_ERR_SHAPE;
+    if (M > kMaxElems / K)
+        return BITLINEAR_ERR_SHAPE;
+    return BITLINEAR_OK;
+}
+
+int check_nk(int64_t N, int64_t K)
+{
+    if (N < 1 || N > INT32_MAX || K < 4 || K > BITLINEAR_MAX_K || (K % 4) != 0)
+        return BITLINEAR_ERR_SHAPE;
+    if (N > kMaxElems / K)
+        return BITLINEAR_ERR_SHAPE;
+    return BITLINEAR_OK;
+}
+
+int launched()
+{
+    return hipGetLastError() == hipSuccess ? BITLINEAR_OK : BITLINEAR_ERR_HIP;
+}
+
+// Level sizes of the |W| reduction tree (4096 -> 1 per block, repeated).
+int64_t sum_levels(int64_t n, int64_t* sizes, int max_levels, int* nlev)
+{
+    int64_t total = 0;
+    int l = 0;
+    int64_t cur = n;
+    do {
+        cur = (cur + bl::kSumChunk - 1) / bl::kSumChunk;
+        if (l < max_levels)
+            sizes[l] = cur;
+        total += cur;
+        ++l;
+    } while (cur > 1);
+    *nlev = l;
+    return total;
+}
+
+// ---------------------------------------------------------------------- forward dispatch
+
+template <int L, int MT, bool FUSED>
+void launch_k64(const bl::FwdArgs& a, hipStream_t stream)
+{
+    constexpr int RPW = 256 / L;
+    const int64_t passes = (a.N + RPW - 1) / RPW;
+    const int64_t tiles = (a.M + MT - 1) / MT;
+    const int64_t max_x = int64_t(cu_count()) * 4;
+    const int gx = (int)(passes < max_x ? passes : max_x);
+    const int gy = (int)(tiles < 65535 ? tiles : 65535);
+    hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, FUSED>), dim3(gx, gy), dim3(256), 0, stream, a);
+}
+
+template <int MT, bool FUSED>
+bool dispatch_l(const bl::FwdArgs& a, hipStream_t stream)
+{
+    constexpr int CPL = 4 / MT;
+    const int KC = a.K / 64;
+    if (KC <= 8 * CPL) { launch_k64<8, MT, FUSED>(a, stream); return true; }
+    if (KC <= 16 * CPL) { launch_k64<16, MT, FUSED>(a, stream); return true; }
+    if (KC <= 32 * CPL) { launch_k64<32, MT, FUSED>(a, stream); return true; }
+    if (KC <= 64 * CPL) { launch_k64<64, MT, FUSED>(a, stream); return true; }
+    if (KC <= 128 * CPL) { launch_k64<128, MT, FUSED>(a, stream); return true; }
+    if (KC <= 256 * CPL) { launch_k64<256, MT, FUSED>(a, stream); return true; }
+    return false;
+}
+
+template <bool FUSED>
+void launch_generic(const bl::FwdArgs& a, hipStream_t stream)
+{
+    const int64_t passes = (a.N + 3) / 4;
+    const int64_t tiles = (a.M + 3) / 4;
+    const int64_t max_x = int64_t(cu_count()) * 4;
+    const int gx = (int)(passes < max_x ? passes : max_x);
+    const int gy = (int)(tiles < 65535 ? tiles : 65535);
+    hipLaunchKernelGGL((bl::gemv_generic_kernel<FUSED>), dim3(gx, gy), dim3(256), 0, stream, a);
+}
+
+template <bool FUSED>
+void dispatch_forward(const bl::FwdArgs& a, bool chunk_ok, hipStream_t stream)
+{
+    if (chunk_ok) {
+        if (a.M == 1 && dispatch_l<1, FUSED>(a, stream))
+            return;
+        if (a.M == 2 && dispatch_l<2, FUSED>(a, stream))
+            return;
+        if (a.M >= 3 && dispatch_l<4, FUSED>(a, stream))
+            return;
+        if (a.M >= 2 && dispatch_l<2, FUSED>(a, stream))
+            return;
+        if (dispatch_l<1, FUSED>(a, stream))
+            return;
+    }
+    launch_generic<FUSED>(a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bitlinear_status_string(int status)
+{
+    switch (status) {
+    case BITLINEAR_OK: return "ok";
+    case BITLINEAR_ERR_NULL: return "a required pointer is NULL";
+    case BITLINEAR_ERR_SHAPE: return "a size is out of range or K is not a multiple of 4";
+    case BITLINEAR_ERR_ALIGN: return "a pointer is not aligned as required";
+    case BITLINEAR_ERR_WORKSPACE: return "workspace is smaller than bitlinear_pack_workspace_bytes";
+    case BITLINEAR_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+    case BITLINEAR_ERR_HIP: return "the HIP runtime rejected a launch";
+    default: return "unknown status";
+    }
+}
+
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K)
+{
+    if (check_nk(N, K) != BITLINEAR_OK)
+        return 0;
+    int64_t sizes[16];
+    int nlev = 0;
+    return (size_t)sum_levels(N * K, sizes, 16, &nlev) * sizeof(double);
+}
+
+int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* W_packed, float* gamma,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!W || !W_packed || !gamma || !workspace)
+        return BITLINEAR_ERR_NULL;
+    int st = check_nk(N, K);
+    if (st != BITLINEAR_OK)
+        return st;
+    if (!aligned(W, 16) || !aligned(W_packed, 4) || !aligned(gamma, 4) || !aligned(workspace, 8))
+        return BITLINEAR_ERR_ALIGN;
+    const int64_t n = N * K;
+    int64_t sizes[16];
+    int nlev = 0;
+    const int64_t need = sum_levels(n, sizes, 16, &nlev) * (int64_t)sizeof(double);
+    if ((int64_t)workspace_bytes < need)
+        return BITLINEAR_ERR_WORKSPACE;
+    if (overlap(W_packed, n / 4, W, n * 4) || overlap(gamma, 4, W, n * 4) || overlap(workspace, need, W, n * 4) ||
+        overlap(W_packed, n / 4, workspace, need) || overlap(gamma, 4, workspace, need) ||
+        overlap(gamma, 4, W_packed, n / 4))
+        return BITLINEAR_ERR_ALIAS;
+
+    double* ws = static_cast<double*>(workspace);
+    hipLaunchKernelGGL(bl::abs_sum_f32_kernel, dim3((unsigned)sizes[0]), dim3(256), 0, stream, W, n, ws);
+    if ((st = launched()) != BITLINEAR_OK)
+        return st;
+    double* in = ws;
+    for (int l = 1; l < nlev; ++l) {
+        double* out = in + sizes[l - 1];
+        hipLaunchKernelGGL(bl::sum_f64_kernel, dim3((unsigned)sizes[l]), dim3(256), 0, stream,
+                           (const double*)in, sizes[l - 1], out);
+        if ((st = launched()) != BITLINEAR_OK)
+            return st;
+        in = out;
+    }
+    const int64_t nwords = (n / 4 + 3) / 4;
+    const int64_t blocks = (nwords + 255) / 256;
+    const int64_t max_blocks = int64_t(cu_count()) * 16;
+    hipLaunchKernelGGL(bl::quant_pack_kernel, dim3((unsigned)(blocks < max_blocks ? blocks : max_blocks)), dim3(256),
+                       0, stream, W, n, (const double*)in, gamma, W_packed);
+    return launched();
+}
+
+int bitlinear_quantize_act(const float* X, int64_t M, int64_t K, const float* gain, float eps, int relu2,
+                           int8_t* Xq, float* x_scale, hipStream_t stream)
+{
+    if (!X || !Xq || !x_scale)
+        return BITLINEAR_ERR_NULL;
+    int st = check_mk(M, K);
+    if (st != BITLINEAR_OK)
+        return st;
+    if (!aligned(X, 16) || !aligned(Xq, 4) || !aligned(x_scale, 4) || (gain && !aligned(gain, 16)))
+        return BITLINEAR_ERR_ALIGN;
+    if (overlap(Xq, M * K, X, M * K * 4) || overlap(x_scale, M * 4, X, M * K * 4) ||
+        overlap(Xq, M * K, gain, K * 4) || overlap(x_scale, M * 4, gain, K * 4) || overlap(Xq, M * K, x_scale, M * 4))
+        return BITLINEAR_ERR_ALIAS;
+    bl::QuantArgs a{X, gain, Xq, x_scale, M, (int)K, eps, relu2 ? 1 : 0};
+    const int64_t max_blocks = int64_t(cu_count()) * 64;
+    hipLaunchKernelGGL(bl::quantize_act_kernel, dim3((unsigned)(M < max_blocks ? M : max_blocks)), dim3(256), 0,
+                       stream, a);
+    return launched();
+}
+
+int bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed,
+                      const float* gamma, int64_t N, float* Y, int32_t* acc, hipStream_t stream)
+{
+    if (!Xq || !x_scale || !W_packed || !gamma || !Y)
+        return BITLINEAR_ERR_NULL;
+    int st = check_mk(M, K);
+    if (st != BITLINEAR_OK)
+        return st;
+    if ((st = check_nk(N, K)) != BITLINEAR_OK)
+        return st;
+    if (M > kMaxElems / N)
+        return BITLINEAR_ERR_SHAPE;
+    if (!aligned(Xq, 4) || !aligned(x_scale, 4) || !aligned(W_packed, 1) || !aligned(gamma, 4) ||
+        !aligned(Y, 4) || (acc && !aligned(acc, 4)))
+        return BITLINEAR_ERR_ALIGN;
+    const int64_t ybytes = M * N * 4;
+    const void* ins[4] = {Xq, x_scale, W_packed, gamma};
+    const int64_t insz[4] = {M * K, M * 4, N * (K / 4), 4};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(Y, ybytes, ins[i], insz[i]) || overlap(acc, ybytes, ins[i], insz[i]))
+            return BITLINEAR_ERR_ALIAS;
+    if (overlap(Y, ybytes, acc, ybytes))
+        return BITLINEAR_ERR_ALIAS;
+    bl::FwdArgs a{};
+    a.Xq = Xq;
+    a.xscale = x_scale;
+    a.W = W_packed;
+    a.gamma = gamma;
+    a.Y = Y;
+    a.acc = acc;
+    a.M = M;
+    a.N = N;
+    a.K = (int)K;
+    const bool chunk_ok = (K % 64) == 0 && aligned(W_packed, 16) && aligned(Xq, 16);
+    dispatch_forward<false>(a, chunk_ok, stream);
+    return launched();
+}
+
+int bitlinear_forward_f32(const float* X, int64_t M, int64_t K, const float* gain, float eps, int relu2,
+                          const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, hipStream_t stream)
+{
+    if (!X || !W_packed || !gamma || !Y)
+        return BITLINEAR_ERR_NULL;
+    int st = check_mk(M, K);
+    if (st != BITLINEAR_OK)
+        return st;
+    if ((st = check_nk(N, K)) != BITLINEAR_OK)
+        return st;
+    if (M > kMaxElems / N)
+        return BITLINEAR_ERR_SHAPE;
+    if (!aligned(X, 16) || (gain && !aligned(gain, 16)) || !aligned(gamma, 4) || !aligned(Y, 4))
+        return BITLINEAR_ERR_ALIGN;
+    const int64_t ybytes = M * N * 4;
+    const void* ins[4] = {X, gain, W_packed, gamma};
+    const int64_t insz[4] = {M * K * 4, K * 4, N * (K / 4), 4};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(Y, ybytes, ins[i], insz[i]))
+            return BITLINEAR_ERR_ALIAS;
+    bl::FwdArgs a{};
+    a.X = X;
+    a.gain = gain;
+    a.eps = eps;
+    a.relu2 = relu2 ? 1 : 0;
+    a.W = W_packed;
+    a.gamma = gamma;
+    a.Y = Y;
+    a.M = M;
+    a.N = N;
+    a.K = (int)K;
+    const bool chunk_ok = (K % 64) == 0 && aligned(W_packed, 16);
+    dispatch_forward<true>(a, chunk_ok, stream);
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// device_common.hpp -- small device helpers shared by the BitLinear kernels (gfx950).
+//
+// Wave64 throughout. Every reduction here is either order-free (max, integer sums) or
+// follows a fixed tree that depends only on the problem size, never on timing, so
+// repeated calls and the fused/unfused entry points give identical bits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+constexpr float kFloor = 1e-8f;  // floor of max|x| and of gamma
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+// int8 code of one activation: clip(round_half_even(v * s), -128, 127). One fp32
+// multiply, v_rndne_f32, then a clamp.
+__device__ __forceinline__ int act_code(float v, float s)
+{
+    float r = __builtin_rintf(v * s);
+    r = r > 127.0f ? 127.0f : r;
+    r = r < -128.0f ? -128.0f : r;
+    return (int)r;
+}
+
+// Elementwise part of the subln input: squared ReLU (optional), then the gain.
+__device__ __forceinline__ float pre_v(float u, int relu2)
+{
+    if (relu2) {
+        float p = u > 0.0f ? u : 0.0f;
+        return p * p;
+    }
+    return u;
+}
+
+// Byte-transpose of four dwords: out[f] byte j = in[j] byte f.
+__device__ __forceinline__ void transpose_bytes(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3,
+                                                uint32_t out[4])
+{
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int s = 8 * f;
+        out[f] = ((e0 >> s) & 0xffu) | (((e1 >> s) & 0xffu) << 8) | (((e2 >> s) & 0xffu) << 16) |
+                 (((e3 >> s) & 0xffu) << 24);
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Per-token statistics of the (optional ReLU^2 + gain) input, shared by the standalone
+// quantizer and the fused GEMV prologue so that both produce the same bits.
+//
+//   m     = max_k |w_k|,  w_k = pre_v(u_k) * gain_k   (order-free)
+//   sumsq = sum_k v_k^2 in binary64 over 256 virtual lanes: virtual lane l adds the
+//           float4 groups g = l, l+256, l+512, ... in increasing order (components in
+//           order), then the 256 lane sums are combined as a pairwise tree in lane
+//           order. The tree is independent of the real block size NT (64 or 256).
+// Must be called by all NT threads of the block (it synchronizes the block).
+// ------------------------------------------------------------------------------------
+struct RowStats {
+    float m;
+    double sumsq;
+};
+
+template <int NT>
+__device__ RowStats row_stats(const float* __restrict__ u, int K, const float* __restrict__ gain, int relu2,
+                              bool want_sumsq)
+{
+    static_assert(NT == 64 || NT == 256, "row_stats supports 64- or 256-thread blocks");
+    constexpr int V = 256 / NT;
+    const int tid = threadIdx.x;
+    const int G = K >> 2;
+    double part[V];
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        double s = 0.0;
+        for (int g = tid + i * NT; g < G; g += 256) {
+            const float4 a = reinterpret_cast<const float4*>(u)[g];
+            float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            if (gain)
+                gv = reinterpret_cast<const float4*>(gain)[g];
+            const float va[4] = {a.x, a.y, a.z, a.w};
+            const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float v = pre_v(va[c], relu2);
+                if (want_sumsq)
+                    s += (double)v * (double)v;
+                const float w = gain ? v * ga[c] : v;
+                mx = fmaxf(mx, fabsf(w));
+            }
+        }
+        part[i] = s;
+    }
+    // max over the block (exact in any order)
+    mx = wave_max(mx);
+    __shared__ float redm[NT / kWave];
+    __shared__ double red[NT / kWave];
+    const int wv = tid / kWave;
+    if ((tid & (kWave - 1)) == 0)
+        redm[wv] = mx;
+    double total = 0.0;
+    if (want_sumsq) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+#pragma unroll
+            for (int m = 1; m < kWave; m <<= 1)
+                part[i] += __shfl_xor(part[i], m);
+        }
+        // part[i] now holds the sum of virtual wave (wv + i * NT/64)
+        if constexpr (NT == 256) {
+            if ((tid & (kWave - 1)) == 0)
+                red[wv] = part[0];
+        }
+    }
+    __syncthreads();
+    float m = redm[0];
+#pragma unroll
+    for (int w = 1; w < NT / kWave; ++w)
+        m = fmaxf(m, redm[w]);
+    if (want_sumsq) {
+        if constexpr (NT == 256)
+            total = (red[0] + red[1]) + (red[2] + red[3]);
+        else
+            total = (part[0] + part[1]) + (part[2] + part[3]);
+    }
+    __syncthreads();  // LDS scratch may be reused by the caller
+    return RowStats{m, total};
+}
+
+// Scales of one token from its statistics: s' multiplies w to give the codes; the
+// stored scale s is that of the normalized activation (s' * sqrt(mean v^2 + eps)).
+__device__ __forceinline__ void token_scales(const RowStats& st, int K, bool norm, float eps, float& sp, float& s)
+{
+    const float m = st.m < kFloor ? kFloor : st.m;
+    sp = 127.0f / m;
+    if (norm) {
+        const double ms = st.sumsq / (double)K;
+        s = (float)((double)sp * sqrt(ms + (double)eps));
+    } else {
+        s = sp;
+    }
+}
+
+}  // namespace bl

@@ -1,0 +1,58 @@
+// quant.hpp -- per-token absmax int8 activation quantization (optionally with the
+// squared-ReLU + RMSNorm subln input), one 256-thread block per token.
+//
+// Absmax per token with scale 127/max(|x|, 1e-8), round, clamp to [-128, 127]:
+// "BitNet b1.58 深度解析" s.2.2 and, for the per-token granularity, "微软AI大模型炸场"
+// s.1 and "20亿参数仅0.4GB" s.2. The subln input folds the RMSNorm factor into the
+// stored scale (the factor cancels inside absmax), so the codes are order-free.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace bl {
+
+struct QuantArgs {
+    const float* X;
+    const float* gain;
+    int8_t* Xq;
+    float* scale;
+    int64_t M;
+    int K;
+    float eps;
+    int relu2;
+};
+
+// Pass 1: block statistics of the token. Pass 2: codes, four per 32-bit store; the
+// row is re-read (it is L2-resident after pass 1).
+__global__ __launch_bounds__(256) void quantize_act_kernel(QuantArgs a)
+{
+    for (int64_t t = blockIdx.x; t < a.M; t += gridDim.x) {
+        const float* u = a.X + t * (int64_t)a.K;
+        const bool norm = a.gain != nullptr;
+        const RowStats st = row_stats<256>(u, a.K, a.gain, a.relu2, norm);
+        float sp, s;
+        token_scales(st, a.K, norm, a.eps, sp, s);
+        if (threadIdx.x == 0)
+            a.scale[t] = s;
+        uint32_t* out = reinterpret_cast<uint32_t*>(a.Xq + t * (int64_t)a.K);
+        const int G = a.K >> 2;
+        for (int g = threadIdx.x; g < G; g += 256) {
+            const float4 x = reinterpret_cast<const float4*>(u)[g];
+            float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            if (a.gain)
+                gv = reinterpret_cast<const float4*>(a.gain)[g];
+            const float xa[4] = {x.x, x.y, x.z, x.w};
+            const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
+            uint32_t word = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float v = pre_v(xa[c], a.relu2);
+                const float w = a.gain ? v * ga[c] : v;
+                word |= (uint32_t)(act_code(w, sp) & 0xff) << (8 * c);
+            }
+            out[g] = word;
+        }
+    }
+}
+
+}  // namespace bl

@@ -1,0 +1,125 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments with a status code before any HIP call
+(the pointers passed below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_linear_w1_amd as bl
+from ternary_weight_linear_w1_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = range(7)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not _build.up_to_date():
+        _build.build()
+    return bl.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", src)))
+
+
+def P(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) == set(bl.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert bl.status_string(s)
+    assert bl.status_string(99) == "unknown status"
+
+
+def test_pack_workspace_bytes(L):
+    def expect(n):
+        total, cur = 0, n
+        while True:
+            cur = -(-cur // 4096)
+            total += cur
+            if cur == 1:
+                return total * 8
+    for N, K in [(1, 4), (64, 64), (2560, 2560), (28672, 8192), (4096, 4100)]:
+        assert bl.bitlinear_pack_workspace_bytes(N, K) == expect(N * K)
+    assert bl.bitlinear_pack_workspace_bytes(3, 6) == 0
+    assert bl.bitlinear_pack_workspace_bytes(0, 4) == 0
+
+
+def test_forward_rejects_before_launch(L):
+    f = L.bitlinear_forward
+    a = 1 << 20
+    args = dict(Xq=P(a), s=P(2 * a), M=1, K=64, W=P(3 * a), g=P(4 * a), N=8, Y=P(5 * a), acc=None, st=None)
+
+    def call(**kw):
+        d = dict(args, **kw)
+        return f(d["Xq"], d["s"], d["M"], d["K"], d["W"], d["g"], d["N"], d["Y"], d["acc"], d["st"])
+    assert call(Xq=None) == ERR_NULL
+    assert call(Y=None) == ERR_NULL
+    assert call(g=None) == ERR_NULL
+    assert call(K=6) == ERR_SHAPE
+    assert call(K=0) == ERR_SHAPE
+    assert call(M=0) == ERR_SHAPE
+    assert call(N=0) == ERR_SHAPE
+    assert call(N=1 << 31) == ERR_SHAPE
+    assert call(K=(1 << 20) + 4) == ERR_SHAPE
+    assert call(Y=P(5 * a + 2)) == ERR_ALIGN
+    assert call(Xq=P(a + 1)) == ERR_ALIGN
+    assert call(Y=P(3 * a)) == ERR_ALIAS
+    assert call(acc=P(5 * a)) == ERR_ALIAS
+
+
+def test_forward_f32_rejects_before_launch(L):
+    f = L.bitlinear_forward_f32
+    a = 1 << 20
+    assert f(None, 1, 64, None, 1e-5, 0, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_NULL
+    assert f(P(a), 1, 62, None, 1e-5, 0, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_SHAPE
+    assert f(P(a + 4), 1, 64, None, 1e-5, 0, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_ALIGN
+    assert f(P(a), 1, 64, P(2 * a + 8), 1e-5, 0, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_ALIGN
+    assert f(P(a), 1, 64, None, 1e-5, 0, P(3 * a), P(4 * a), 8, P(a), None) == ERR_ALIAS
+
+
+def test_quantize_act_rejects_before_launch(L):
+    f = L.bitlinear_quantize_act
+    a = 1 << 20
+    assert f(None, 1, 64, None, 1e-5, 0, P(2 * a), P(3 * a), None) == ERR_NULL
+    assert f(P(a), 1, 66, None, 1e-5, 0, P(2 * a), P(3 * a), None) == ERR_SHAPE
+    assert f(P(a), 0, 64, None, 1e-5, 0, P(2 * a), P(3 * a), None) == ERR_SHAPE
+    assert f(P(a + 8), 1, 64, None, 1e-5, 0, P(2 * a), P(3 * a), None) == ERR_ALIGN
+    assert f(P(a), 1, 64, None, 1e-5, 0, P(a + 16), P(3 * a), None) == ERR_ALIAS
+
+
+def test_pack_rejects_before_launch(L):
+    f = L.bitlinear_pack_weights
+    a = 1 << 24
+    ws = bl.bitlinear_pack_workspace_bytes(16, 64)
+    assert f(None, 16, 64, P(2 * a), P(3 * a), P(4 * a), ws, None) == ERR_NULL
+    assert f(P(a), 16, 64, P(2 * a), P(3 * a), None, ws, None) == ERR_NULL
+    assert f(P(a), 16, 66, P(2 * a), P(3 * a), P(4 * a), ws, None) == ERR_SHAPE
+    assert f(P(a), 16, 64, P(2 * a), P(3 * a), P(4 * a), ws - 8, None) == ERR_WORKSPACE
+    assert f(P(a + 4), 16, 64, P(2 * a), P(3 * a), P(4 * a), ws, None) == ERR_ALIGN
+    assert f(P(a), 16, 64, P(a + 64), P(3 * a), P(4 * a), ws, None) == ERR_ALIAS
+
+
+def test_binding_without_gpu_fails_loudly():
+    """Without a device the binding must raise, never compute on the CPU."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    w = torch.zeros((4, 8))
+    with pytest.raises(ValueError):
+        bl.bitlinear_pack_weights(w)

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Bar: packed bytes, gamma, activation codes, plain-path scales and int32 accumulators
+bit-exact; fp32 outputs bit-exact on the plain path; on the RMSNorm (subln) path the
+scale's binary64 sum is summed in a different order than the oracle's, so scales may
+differ by an ulp and y is held to 1e-6 relative (the tolerance the method's target
+states). The fused entry point must equal quantize + forward bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import ternary_weight_linear_w1_amd as bl
+from ternary_weight_linear_w1_amd import _build
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+EPS = 1e-5
+F32 = np.float32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not _build.up_to_date():
+        _build.build()
+    bl.lib()
+    oracle.lib()
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+
+
+def up(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def down(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def ulp_diff(a, b):
+    a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(a - b)
+
+
+def latents(n, k, seed, kind="gg"):
+    if kind == "gauss":
+        return datagen.gaussian_weights(n, k, seed)
+    return datagen.gg_weights(n, k, seed)
+
+
+# ------------------------------------------------------------------------------ packing
+
+PACK_SHAPES = [(1, 4, "gauss"), (3, 64, "gg"), (37, 260, "gg"), (64, 2560, "gauss"), (5, 4100, "gg"),
+               (2560, 2560, "gauss"), (3840, 2560, "gg"), (4096, 4100, "gg")]
+
+
+@pytest.mark.parametrize("N,K,kind", PACK_SHAPES)
+def test_pack_parity(N, K, kind):
+    w = latents(N, K, 1000 + N + K, kind)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    opacked, ogamma, _ = oracle.pack_weights(w)
+    assert down(gamma)[0] == ogamma
+    assert np.array_equal(down(packed), opacked)
+
+
+def test_pack_golden_and_degenerate(golden):
+    g = golden["weight_ties"]
+    packed, gamma = bl.bitlinear_pack_weights(up(np.array(g["W"], np.float32)))
+    assert down(gamma)[0] == F32(g["gamma"])
+    assert down(packed).tolist() == g["packed"]
+    z = np.zeros((9, 36), np.float32)
+    packed, gamma = bl.bitlinear_pack_weights(up(z))
+    assert down(gamma)[0] == F32(1e-8)
+    assert (down(packed) == 0x55).all()          # every field is code 0 -> 0b01
+    # huge dynamic range: a single large weight dominates gamma
+    w = latents(16, 64, 7)
+    w[3, 5] = 1e6
+    opacked, ogamma, _ = oracle.pack_weights(w)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    assert down(gamma)[0] == ogamma and np.array_equal(down(packed), opacked)
+
+
+def test_pack_reuses_workspace_and_is_deterministic():
+    w = up(latents(300, 520, 8))
+    ws = torch.empty((bl.bitlinear_pack_workspace_bytes(300, 520),), dtype=torch.uint8, device=DEV)
+    p1, g1 = bl.bitlinear_pack_weights(w, workspace=ws)
+    p2, g2 = bl.bitlinear_pack_weights(w, workspace=ws)
+    assert torch.equal(p1, p2) and torch.equal(g1, g2)
+
+
+# ------------------------------------------------------------------------------ activations
+
+QUANT_CASES = [
+    (1, 4, None), (3, 260, None), (5, 2560, "norm"), (7, 6912, "relu2norm"), (4, 64, "relu2"),
+    (64, 2560, None), (512, 6912, None), (16, 28672, "relu2norm"), (33, 8192, "norm"),
+]
+
+
+def make_acts(M, K, seed, heavy=False):
+    return datagen.heavy_channel_acts(M, K, seed) if heavy else datagen.outlier_acts(M, K, seed)
+
+
+def pro_args(mode, K, seed):
+    gain = datagen.gains(K, seed) if mode in ("norm", "relu2norm") else None
+    relu2 = mode in ("relu2", "relu2norm")
+    return gain, relu2
+
+
+@pytest.mark.parametrize("M,K,mode", QUANT_CASES)
+def test_quantize_act_parity(M, K, mode):
+    x = make_acts(M, K, 2000 + M + K, heavy=(M >= 64))
+    if M > 2:
+        x[0, :] = 0.0                           # an all-zero token takes the 1e-8 floor
+    gain, relu2 = pro_args(mode, K, 3000 + K)
+    xq, s = bl.bitlinear_quantize_act(up(x), None if gain is None else up(gain), EPS, relu2)
+    if mode is None:
+        oxq, os_ = oracle.quantize_act(x)
+    else:
+        oxq, os_ = oracle.quantize_act_norm(x, gain, EPS, relu2)
+    assert np.array_equal(down(xq), oxq)
+    if gain is None:
+        assert np.array_equal(down(s), os_)
+    else:
+        assert ulp_diff(down(s), os_).max() <= 2
+
+
+def test_quantize_act_golden(golden):
+    g = golden["act_quant"]
+    xq, s = bl.bitlinear_quantize_act(up(np.array(g["X"], np.float32)))
+    assert down(xq).tolist() == g["codes"] and down(s).tolist() == g["scale"]
+    g = golden["relu2_norm"]
+    xq, s = bl.bitlinear_quantize_act(up(np.array(g["U"], np.float32)), up(np.array(g["gain"], np.float32)),
+                                      g["eps"], True)
+    assert down(xq).tolist() == g["codes"]
+
+
+# ------------------------------------------------------------------------------ forward
+
+def run_gpu(x, w, mode=None, gain=None, relu2=False):
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    xg = up(x)
+    gg = None if gain is None else up(gain)
+    if mode is None:
+        xq, s = bl.bitlinear_quantize_act(xg)
+    else:
+        xq, s = bl.bitlinear_quantize_act(xg, gg, EPS, relu2)
+    y, acc = bl.bitlinear_forward(xq, s, packed, gamma, acc=True)
+    yf = bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, relu2)
+    return dict(packed=down(packed), gamma=down(gamma)[0], xq=down(xq), s=down(s), y=down(y), acc=down(acc),
+                yf=down(yf))
+
+
+def compare(r, o, norm):
+    assert r["gamma"] == o["gamma"]
+    assert np.array_equal(r["packed"], o["packed"])
+    assert np.array_equal(r["xq"], o["xq"])
+    assert np.array_equal(r["acc"], o["acc"])
+    assert np.array_equal(r["y"].view(np.int32), r["yf"].view(np.int32)), "fused != quantize+forward"
+    if not norm:
+        assert np.array_equal(r["s"], o["s"])
+        assert np.array_equal(r["y"].view(np.int32), o["y"].view(np.int32))
+    else:
+        yo = o["y"].astype(np.float64)
+        err = np.abs(r["y"].astype(np.float64) - yo)
+        assert (err <= 1e-6 * np.abs(yo)).all()
+
+
+FWD_CASES = [
+    # (M, N, K, mode)  small shapes: several tiles and ragged tails
+    (1, 1, 4, None), (1, 7, 64, None), (2, 37, 260, None), (3, 96, 2560, None), (4, 64, 6912, "norm"),
+    (5, 33, 128, "relu2"), (8, 129, 2560, "relu2norm"), (16, 100, 1024, None), (64, 70, 8192, "norm"),
+    (1, 300, 28672, "relu2norm"), (2, 17, 16384, None), (3, 5, 65536, None), (6, 40, 192, None),
+    (1, 2560, 2560, None),
+]
+
+
+@pytest.mark.parametrize("M,N,K,mode", FWD_CASES)
+def test_forward_parity(M, N, K, mode):
+    w = latents(N, K, 4000 + N * 7 + K)
+    x = make_acts(M, K, 5000 + M + K)
+    gain, relu2 = pro_args(mode, K, 6000 + K)
+    r = run_gpu(x, w, mode, gain, relu2)
+    o = oracle.bitlinear(x, w, gain=gain, eps=EPS, relu2=relu2) if mode else oracle.bitlinear(x, w)
+    compare(r, o, gain is not None)
+
+
+def test_forward_degenerate():
+    """All-zero activations give y = 0; all-zero weights give y = 0; one-hot input."""
+    w = latents(40, 256, 11)
+    x = np.zeros((3, 256), np.float32)
+    x[1, 17] = -3.25
+    r = run_gpu(x, w)
+    o = oracle.bitlinear(x, w)
+    compare(r, o, False)
+    assert (r["y"][0] == 0).all() and (r["y"][2] == 0).all()
+    r = run_gpu(make_acts(2, 256, 12), np.zeros((40, 256), np.float32))
+    assert (r["y"] == 0).all() and (r["acc"] == 0).all()
+
+
+def test_forward_misaligned_views():
+    """Row strides that are not multiples of 16 bytes and offset views take the generic path."""
+    w = latents(21, 68, 13)
+    x = make_acts(3, 68, 14)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    big = torch.zeros(packed.numel() + 1, dtype=torch.uint8, device=DEV)
+    off = big[1:].view(packed.shape)
+    off.copy_(packed)
+    xq, s = bl.bitlinear_quantize_act(up(x))
+    y1 = bl.bitlinear_forward(xq, s, packed, gamma)
+    y2 = bl.bitlinear_forward(xq, s, off, gamma)
+    assert torch.equal(y1, y2)
+    o = oracle.bitlinear(x, w)
+    assert np.array_equal(down(y1), o["y"])
