@@ -1,0 +1,453 @@
+#!/usr/bin/env python3
+"""Benchmark of the W1.58A8 BitLinear forward on one MI355X.
+
+Headline (`value`): HBM GB/s at M = 1 over one step = the four BitLinears of one
+BitNet-b1.58-2B-shaped layer at decode,
+    QKV 2560->3840 (plain absmax input), O 2560->2560 (subln RMSNorm input),
+    up 2560->6912 (plain), down 6912->2560 (ReLU^2 + subln RMSNorm input),
+each one launch of bitlinear_forward_f32 (input quantization fused), weights
+rotated over enough copies (>= 1 GiB) that every step streams them from HBM.
+Bytes per BitLinear = N*K/4 packed weights + 4 (gamma) + 4*M*K fp32 input
+[+ 4*K gain] + 4*M*N fp32 output.
+
+Also printed in the same JSON line:
+  roofline      the dominant kernel of the step (down projection) timed with HIP
+                events on the launch stream, vs 8 TB/s; `traffic` from committed
+                rocprofv3 FETCH_SIZE / WRITE_SIZE counters when they match the
+                current kernel source, else null.
+  cpu_baseline  the CPU oracle on the same layer at M = 1 (single thread).
+  extra         per-matrix kernel rates for the 2B layer at M in {1,4,8}, the
+                100B-shaped slice at M in {1,64}, prefill at M in {512,2048}
+                (int8 TOPS), and the packing rate.
+
+Other modes:
+  --profile roofline   only the dominant kernel plus a copy kernel of known size
+                       (for rocprofv3 --pmc runs);
+  --summarize-pmc F W  turn two rocprofv3 counter CSVs into profiles/ text.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W1.58A8 BitLinear: GEMV HBM GB/s (%peak) @M=1; int8 TOPS (%peak) @M=2048"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+EPS = 1e-5
+ROTATE_BYTES = 1 << 30
+
+# (name, N, K, input mode) of a BitNet-b1.58-2B-shaped layer (hidden 2560, FFN 6912,
+# 20 query heads and 5 key/value heads of 128)
+LAYER_2B = [("qkv", 3840, 2560, "plain"), ("o", 2560, 2560, "norm"), ("up", 6912, 2560, "plain"),
+            ("down", 2560, 6912, "relu2norm")]
+# 100B-shaped layer (hidden 8192, FFN 28672)
+LAYER_100B = [("qkv", 10240, 8192, "plain"), ("o", 8192, 8192, "norm"), ("up", 28672, 8192, "plain"),
+              ("down", 8192, 28672, "relu2norm")]
+
+DOMINANT = "down"
+KERNEL_SRC = ["ternary_weight_linear_w1_amd/csrc/gemv.hpp", "ternary_weight_linear_w1_amd/csrc/device_common.hpp",
+              "ternary_weight_linear_w1_amd/csrc/bitlinear_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_down_2B_M1_traffic.txt")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SRC:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def layer_bytes(N, K, M, mode, fused=True):
+    b = N * K // 4 + 4 + 4 * M * N
+    b += 4 * M * K if fused else (M * K + 4 * M)
+    if mode in ("norm", "relu2norm") and fused:
+        b += 4 * K
+    return b
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- setup
+
+class Mat:
+    """One BitLinear: packed weight copies, gamma, input, gain, output."""
+
+    def __init__(self, torch, bl, datagen, cfg, idx, name, N, K, mode, M, copies, dev):
+        self.name, self.N, self.K, self.mode, self.M = name, N, K, mode, M
+        w = datagen.gg_weights_torch(N, K, datagen.stream_id(cfg, 0, idx, 0), dev)
+        packed, gamma = bl.bitlinear_pack_weights(w)
+        del w
+        self.gamma = gamma
+        self.copies = [packed] + [packed.clone() for _ in range(copies - 1)]
+        self.x = datagen.outlier_acts_torch(M, K, datagen.stream_id(cfg, 0, idx, 1), dev)
+        self.gain = datagen.gains_torch(K, datagen.stream_id(cfg, 0, idx, 2), dev) if "norm" in mode else None
+        self.relu2 = mode == "relu2norm"
+        self.y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        self.xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        self.s = torch.empty((M,), dtype=torch.float32, device=dev)
+
+    def fused(self, bl, c):
+        bl.bitlinear_forward_f32(self.x, self.copies[c], self.gamma, self.gain, EPS, self.relu2, y=self.y)
+
+    def prequant(self, bl):
+        bl.bitlinear_quantize_act(self.x, self.gain, EPS, self.relu2, xq=self.xq, scale=self.s)
+
+    def forward(self, bl, c):
+        bl.bitlinear_forward(self.xq, self.s, self.copies[c], self.gamma, y=self.y)
+
+    def bytes(self, fused=True):
+        return layer_bytes(self.N, self.K, self.M, self.mode, fused)
+
+
+def n_copies(bytes_per_copy, multiple=1):
+    c = max(2, math.ceil(ROTATE_BYTES / bytes_per_copy))
+    return int(math.ceil(c / multiple) * multiple)
+
+
+def time_kernel(torch, fn, copies, reps):
+    """Average duration of one launch: `reps` launches captured back to back in a HIP
+    graph (weight copies rotating), one replay timed with HIP events on the launch
+    stream. The average includes the dispatch gap between consecutive kernels."""
+    for i in range(min(reps, 4)):
+        fn(i % copies)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i % copies)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(layer, seconds=10.0):
+    import numpy as np
+    import datagen
+    import oracle
+    mats = []
+    for idx, (name, N, K, mode) in enumerate(layer):
+        w = datagen.gg_weights(N, K, datagen.stream_id(2, 0, idx, 0))
+        _, gamma, q = oracle.pack_weights(w)
+        x = datagen.outlier_acts(1, K, datagen.stream_id(2, 0, idx, 1))
+        gain = datagen.gains(K, datagen.stream_id(2, 0, idx, 2)) if "norm" in mode else None
+        mats.append((q, gamma, x, gain, mode == "relu2norm", layer_bytes(N, K, 1, mode)))
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        for q, gamma, x, gain, relu2, _ in mats:
+            if gain is None and not relu2:
+                xq, s = oracle.quantize_act(x)
+            else:
+                xq, s = oracle.quantize_act_norm(x, gain, EPS, relu2)
+            oracle.forward(xq, s, q, gamma)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_step = sum(m[5] for m in mats)
+    return {"value": round(per_step * steps / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d steps of the 2B layer's four BitLinears at M=1 (quantize + int32 product + rescale on "
+                      "unpacked codes, plain C, one thread), %.1f s" % (steps, el)}
+
+
+# ----------------------------------------------------------------------------- traffic
+
+def read_traffic():
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
+    import csv
+
+    def per_kernel(path, counter):
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in rows.items()}
+
+    fe = per_kernel(fetch_csv, "FETCH_SIZE")
+    wr = per_kernel(write_csv, "WRITE_SIZE")
+    gk = [k for k in fe if "gemv_k64_kernel" in k]
+    ck = [k for k in fe if "gemv" not in k and ("copy" in k.lower() or "elementwise" in k.lower())]
+    if len(gk) != 1 or not ck:
+        raise SystemExit("could not identify kernels: %s" % list(fe))
+    copyk = max(ck, key=lambda k: fe[k])
+    f_factor = copy_bytes / (fe[copyk] * 1024.0)
+    w_factor = copy_bytes / (wr[copyk] * 1024.0)
+    g_fetch = fe[gk[0]] * 1024.0 * f_factor
+    g_write = wr[gk[0]] * 1024.0 * w_factor
+    N, K, mode = [(n, k, m) for (nm, n, k, m) in LAYER_2B if nm == DOMINANT][0]
+    alg = layer_bytes(N, K, 1, mode)
+    with open(out, "w") as f:
+        f.write("# HBM traffic of the down-projection GEMV (2B layer, 6912->2560, M=1, fused ReLU^2+subln input)\n")
+        f.write("# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by\n")
+        f.write("# the same counter read for a plain copy kernel of %d bytes read and written.\n" % copy_bytes)
+        f.write("# commands:\n")
+        f.write("#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch --output-format csv -- "
+                "python3 bench.py --profile roofline\n")
+        f.write("#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write --output-format csv -- "
+                "python3 bench.py --profile roofline\n")
+        f.write("#   python3 bench.py --summarize-pmc <fetch csv> <write csv>\n")
+        f.write("gemv_kernel = %s\n" % gk[0])
+        f.write("copy_kernel = %s\n" % copyk)
+        f.write("copy_fetch_kib = %.1f\ncopy_write_kib = %.1f\n" % (fe[copyk], wr[copyk]))
+        f.write("fetch_scale = %.4f\nwrite_scale = %.4f\n" % (f_factor, w_factor))
+        f.write("gemv_fetch_kib_raw = %.1f\ngemv_write_kib_raw = %.1f\n" % (fe[gk[0]], wr[gk[0]]))
+        f.write("gemv_fetch_bytes = %d\ngemv_write_bytes = %d\n" % (g_fetch, g_write))
+        f.write("algorithmic_bytes_per_launch = %d\n" % alg)
+        f.write("traffic_bytes_per_launch = %d\n" % (g_fetch + g_write))
+        f.write("kernel_source_sha256_16 = %s\n" % kernel_hash())
+    print(open(out).read())
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--profile", choices=["none", "roofline"], default="none")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary configurations")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--copy-bytes", type=int, default=256 << 20)
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_bytes, TRAFFIC_FILE)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the W1.58A8 BitLinear path here is a single-GPU build "
+              "(no collectives); run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import datagen
+    import ternary_weight_linear_w1_amd as bl
+    from ternary_weight_linear_w1_amd import _build
+
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    bl.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- the 2B layer at M = 1
+    layer_copy_bytes = sum(N * K // 4 for _, N, K, _ in LAYER_2B)
+    G = 8
+    C = n_copies(layer_copy_bytes, G)
+    log("setup: 2B layer, %d rotating weight copies (%.2f GB)" % (C, C * layer_copy_bytes / 1e9))
+    mats = [Mat(torch, bl, datagen, 2, i, *spec, 1, C, dev) for i, spec in enumerate(LAYER_2B)]
+    dom = [m for m in mats if m.name == DOMINANT][0]
+
+    if args.profile == "roofline":
+        for i in range(200):
+            dom.fused(bl, i % C)
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "roofline", "kernel_launches": 200, "copy_bytes": args.copy_bytes}))
+        return 0
+
+    step_bytes = sum(m.bytes() for m in mats)
+
+    def step(c):
+        for m in mats:
+            m.fused(bl, c)
+
+    graphs = []
+    for gi in range(C // G):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in range(gi * G, gi * G + G):
+                step(c)
+        graphs.append(g)
+    singles = {}
+
+    def run_steps(start, count):
+        s = start
+        end = start + count
+        while s < end:
+            c = s % C
+            if c % G == 0 and end - s >= G:
+                graphs[c // G].replay()
+                s += G
+            else:
+                if c not in singles:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        step(c)
+                    singles[c] = g
+                singles[c].replay()
+                s += 1
+        return s
+
+    log("warmup %d steps" % args.warmup)
+    pos = run_steps(0, args.warmup)
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    run_steps(pos, args.steps)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) * 1e-3
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes * args.steps / wall / 1e9
+
+    # ---- roofline of the dominant kernel (down projection), events on the launch stream
+    avg_s = time_kernel(torch, lambda c: dom.fused(bl, c), C, 400)
+    dom_bytes = dom.bytes()
+    achieved = dom_bytes / avg_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
+                "kernel": "bitlinear_forward_f32 down 6912->2560 (ReLU^2+subln input), M=1",
+                "algorithmic_bytes": dom_bytes, "avg_us": round(avg_s * 1e6, 3),
+                "timing": "HIP events around a graph of 400 back-to-back launches on the launch stream"}
+    log("value %.1f GB/s, %.4f ms/step; dominant kernel %.2f us = %.1f GB/s" %
+        (value, ms_per_step, avg_s * 1e6, achieved))
+
+    extra = {"step_bytes": step_bytes, "step_gpu_ms": round(gpu_s / args.steps * 1e3, 5),
+             "weight_copies": C}
+    # per-matrix kernel rates at M = 1 (fused)
+    extra["2B_M1_fused"] = {}
+    for m in mats:
+        a = time_kernel(torch, lambda c, m=m: m.fused(bl, c), C, 200)
+        extra["2B_M1_fused"][m.name] = {"us": round(a * 1e6, 3), "GB/s": round(m.bytes() / a / 1e9, 1)}
+    del graphs, singles
+
+    if not args.no_extra:
+        extra.update(run_extra(torch, bl, datagen, dev, mats))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(LAYER_2B, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "BitNet-b1.58-2B-shaped layer BitLinears at decode, M=1: QKV 2560->3840, "
+                               "O 2560->2560 (subln input), up 2560->6912, down 6912->2560 (ReLU^2+subln input); "
+                               "fused input quantization; GG(0.846) latents (42/29/29 ternary split); "
+                               "%d rotating weight copies so weights stream from HBM" % C,
+                   "M": 1, "entry": "bitlinear_forward_f32", "graph": "HIP graph of 8 steps"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def run_extra(torch, bl, datagen, dev, mats2b):
+    res = {}
+    # ---- 2B layer at M = 4, 8 (pre-quantized forward)
+    for M in (4, 8):
+        C = 16
+        r = {}
+        for i, (name, N, K, mode) in enumerate(LAYER_2B):
+            m = Mat(torch, bl, datagen, 2, 8 + i, name, N, K, mode, M, C, dev)
+            m.prequant(bl)
+            a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), C, 200)
+            b = m.bytes(fused=False)
+            r[name] = {"us": round(a * 1e6, 3), "GB/s": round(b / a / 1e9, 1)}
+            del m
+        res["2B_M%d_forward" % M] = r
+        log("extra 2B M=%d: %s" % (M, r))
+    torch.cuda.empty_cache()
+    # ---- 100B-shaped slice at M = 1 (fused) and M = 64 (pre-quantized)
+    for M in (1, 64):
+        r = {}
+        for i, (name, N, K, mode) in enumerate(LAYER_100B):
+            C = n_copies(N * K // 4)
+            m = Mat(torch, bl, datagen, 5, i + 4 * (M > 1), name, N, K, mode, M, C, dev)
+            if M == 1:
+                a = time_kernel(torch, lambda c, m=m: m.fused(bl, c), C, 100)
+                b = m.bytes()
+            else:
+                m.prequant(bl)
+                a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), C, 100)
+                b = m.bytes(fused=False)
+            ops = 2.0 * M * N * K
+            r[name] = {"us": round(a * 1e6, 2), "GB/s": round(b / a / 1e9, 1), "TOPS": round(ops / a / 1e12, 2)}
+            del m
+            torch.cuda.empty_cache()
+        res["100B_M%d" % M] = r
+        log("extra 100B M=%d: %s" % (M, r))
+    # ---- prefill on the 2B shapes (pre-quantized forward), int8 TOPS
+    for M in (512, 2048):
+        r = {}
+        for i, (name, N, K, mode) in enumerate(LAYER_2B):
+            m = Mat(torch, bl, datagen, 4, i + 4 * (M > 512), name, N, K, mode, M, 2, dev)
+            m.x = datagen.heavy_channel_acts_torch(M, K, datagen.stream_id(4, 1, i, 1), dev)
+            m.prequant(bl)
+            a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), 2, 10)
+            ops = 2.0 * M * N * K
+            r[name] = {"us": round(a * 1e6, 1), "TOPS": round(ops / a / 1e12, 2),
+                       "frac_int8_peak": round(ops / a / 1e12 / INT8_PEAK_TOPS, 4)}
+            del m
+        res["2B_prefill_M%d" % M] = r
+        log("extra prefill M=%d: %s" % (M, r))
+    # ---- packing rate (100B up projection)
+    N, K = 28672, 8192
+    w = datagen.gg_weights_torch(N, K, datagen.stream_id(5, 9, 0, 0), dev)
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+    gamma = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = torch.empty((bl.bitlinear_pack_workspace_bytes(N, K),), dtype=torch.uint8, device=dev)
+    a = time_kernel(torch, lambda c: bl.bitlinear_pack_weights(w, packed, gamma, ws), 1, 5)
+    res["pack_100B_up"] = {"ms": round(a * 1e3, 3), "GB/s (2 reads of W + packed write)":
+                           round((2 * 4 * N * K + N * K // 4) / a / 1e9, 1)}
+    del w, packed, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -88,29 +88,66 @@ int64_t sum_levels(int64_t n, int64_t* sizes, int max_levels, int* nlev)
 
 // ---------------------------------------------------------------------- forward dispatch
 
-template <int L, int MT, bool FUSED>
-void launch_k64(const bl::FwdArgs& a, hipStream_t stream)
+// Launch shapes were chosen by timing back-to-back launches on MI355X for the BitNet
+// 2B (K = 2560, 6912) and 100B (K = 8192, 28672) layer shapes.
+template <int L, int MT, int CPL, int R, bool FUSED>
+void launch_k64(const bl::FwdArgs& a, int wg_per_cu, hipStream_t stream)
 {
-    constexpr int RPW = 256 / L;
-    const int64_t passes = (a.N + RPW - 1) / RPW;
+    constexpr int RPP = (256 / L) * R;
+    const int64_t passes = (a.N + RPP - 1) / RPP;
     const int64_t tiles = (a.M + MT - 1) / MT;
-    const int64_t max_x = int64_t(cu_count()) * 4;
+    const int64_t max_x = int64_t(cu_count()) * wg_per_cu;
     const int gx = (int)(passes < max_x ? passes : max_x);
     const int gy = (int)(tiles < 65535 ? tiles : 65535);
-    hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, FUSED>), dim3(gx, gy), dim3(256), 0, stream, a);
+    const size_t lds = (size_t)MT * (size_t)a.K;
+    hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, R, FUSED>), dim3(gx, gy), dim3(256), lds, stream, a);
 }
 
-template <int MT, bool FUSED>
-bool dispatch_l(const bl::FwdArgs& a, hipStream_t stream)
+// One token per tile: up to 4 chunks (256 codes) per lane.
+template <bool FUSED>
+bool dispatch_mt1(const bl::FwdArgs& a, hipStream_t stream)
 {
-    constexpr int CPL = 4 / MT;
     const int KC = a.K / 64;
-    if (KC <= 8 * CPL) { launch_k64<8, MT, FUSED>(a, stream); return true; }
-    if (KC <= 16 * CPL) { launch_k64<16, MT, FUSED>(a, stream); return true; }
-    if (KC <= 32 * CPL) { launch_k64<32, MT, FUSED>(a, stream); return true; }
-    if (KC <= 64 * CPL) { launch_k64<64, MT, FUSED>(a, stream); return true; }
-    if (KC <= 128 * CPL) { launch_k64<128, MT, FUSED>(a, stream); return true; }
-    if (KC <= 256 * CPL) { launch_k64<256, MT, FUSED>(a, stream); return true; }
+    const bool big = a.N * (int64_t)a.K >= (int64_t(64) << 20);   // >= 16 MB of packed weights
+    if (KC <= 48) { launch_k64<16, 1, 3, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 64) { launch_k64<16, 1, 4, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 128) {
+        if (big) launch_k64<32, 1, 4, 2, FUSED>(a, 2, stream);
+        else launch_k64<32, 1, 4, 1, FUSED>(a, 1, stream);
+        return true;
+    }
+    if (KC <= 256) { launch_k64<64, 1, 4, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 512) { launch_k64<128, 1, 4, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 1024) { launch_k64<256, 1, 4, 1, FUSED>(a, 2, stream); return true; }
+    return false;
+}
+
+// Two tokens per tile: up to 2 chunks per lane.
+template <bool FUSED>
+bool dispatch_mt2(const bl::FwdArgs& a, hipStream_t stream)
+{
+    const int KC = a.K / 64;
+    if (KC <= 32) { launch_k64<16, 2, 2, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 64) { launch_k64<32, 2, 2, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 128) { launch_k64<64, 2, 2, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 256) { launch_k64<128, 2, 2, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 512) { launch_k64<256, 2, 2, 1, FUSED>(a, 2, stream); return true; }
+    return false;
+}
+
+// Four tokens per tile: one chunk per lane.
+template <bool FUSED>
+bool dispatch_mt4(const bl::FwdArgs& a, hipStream_t stream)
+{
+    const int KC = a.K / 64;
+    const bool big = a.N * (int64_t)a.K >= (int64_t(64) << 20);
+    if (KC <= 64) { launch_k64<64, 4, 1, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 128) {
+        if (big) launch_k64<128, 4, 1, 4, FUSED>(a, 2, stream);
+        else launch_k64<128, 4, 1, 1, FUSED>(a, 2, stream);
+        return true;
+    }
+    if (KC <= 256) { launch_k64<256, 4, 1, 1, FUSED>(a, 2, stream); return true; }
     return false;
 }
 
@@ -129,15 +166,15 @@ template <bool FUSED>
 void dispatch_forward(const bl::FwdArgs& a, bool chunk_ok, hipStream_t stream)
 {
     if (chunk_ok) {
-        if (a.M == 1 && dispatch_l<1, FUSED>(a, stream))
+        if (a.M == 1 && dispatch_mt1<FUSED>(a, stream))
             return;
-        if (a.M == 2 && dispatch_l<2, FUSED>(a, stream))
+        if (a.M == 2 && dispatch_mt2<FUSED>(a, stream))
             return;
-        if (a.M >= 3 && dispatch_l<4, FUSED>(a, stream))
+        if (a.M >= 3 && dispatch_mt4<FUSED>(a, stream))
             return;
-        if (a.M >= 2 && dispatch_l<2, FUSED>(a, stream))
+        if (a.M >= 2 && dispatch_mt2<FUSED>(a, stream))
             return;
-        if (dispatch_l<1, FUSED>(a, stream))
+        if (dispatch_mt1<FUSED>(a, stream))
             return;
     }
     launch_generic<FUSED>(a, stream);

@@ -62,6 +62,8 @@ __device__ __forceinline__ void transpose_bytes(uint32_t e0, uint32_t e1, uint32
 //           float4 groups g = l, l+256, l+512, ... in increasing order (components in
 //           order), then the 256 lane sums are combined as a pairwise tree in lane
 //           order. The tree is independent of the real block size NT (64 or 256).
+// With NT == 256 the w values of the first KEEP groups of each thread (g = tid + 256 i,
+// i < KEEP) are returned in `wk` so the caller can quantize them without re-reading.
 // Must be called by all NT threads of the block (it synchronizes the block).
 // ------------------------------------------------------------------------------------
 struct RowStats {
@@ -69,11 +71,12 @@ struct RowStats {
     double sumsq;
 };
 
-template <int NT>
+template <int NT, int KEEP = 0>
 __device__ RowStats row_stats(const float* __restrict__ u, int K, const float* __restrict__ gain, int relu2,
-                              bool want_sumsq)
+                              bool want_sumsq, float4* wk = nullptr)
 {
     static_assert(NT == 64 || NT == 256, "row_stats supports 64- or 256-thread blocks");
+    static_assert(KEEP == 0 || NT == 256, "kept values need one virtual lane per thread");
     constexpr int V = 256 / NT;
     const int tid = threadIdx.x;
     const int G = K >> 2;
@@ -82,21 +85,46 @@ __device__ RowStats row_stats(const float* __restrict__ u, int K, const float* _
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         double s = 0.0;
-        for (int g = tid + i * NT; g < G; g += 256) {
-            const float4 a = reinterpret_cast<const float4*>(u)[g];
-            float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-            if (gain)
-                gv = reinterpret_cast<const float4*>(gain)[g];
+        int g = tid + i * NT;
+        auto visit = [&](float4 a, float4 gv) -> float4 {
             const float va[4] = {a.x, a.y, a.z, a.w};
             const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
+            float wa[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const float v = pre_v(va[c], relu2);
                 if (want_sumsq)
                     s += (double)v * (double)v;
-                const float w = gain ? v * ga[c] : v;
-                mx = fmaxf(mx, fabsf(w));
+                wa[c] = gain ? v * ga[c] : v;
+                mx = fmaxf(mx, fabsf(wa[c]));
             }
+            return make_float4(wa[0], wa[1], wa[2], wa[3]);
+        };
+        if constexpr (KEEP > 0) {
+            float4 xa[KEEP], gb[KEEP];
+#pragma unroll
+            for (int q = 0; q < KEEP; ++q) {
+                const int gq = g + q * 256;
+                xa[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                gb[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                if (gq < G) {
+                    xa[q] = reinterpret_cast<const float4*>(u)[gq];
+                    if (gain)
+                        gb[q] = reinterpret_cast<const float4*>(gain)[gq];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < KEEP; ++q)
+                if (g + q * 256 < G)
+                    wk[q] = visit(xa[q], gb[q]);
+            g += KEEP * 256;
+        }
+        for (; g < G; g += 256) {
+            const float4 a = reinterpret_cast<const float4*>(u)[g];
+            float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            if (gain)
+                gv = reinterpret_cast<const float4*>(gain)[g];
+            visit(a, gv);
         }
         part[i] = s;
     }
