@@ -9,6 +9,7 @@
 
 #include "../../include/bitlinear.h"
 #include "device_common.hpp"
+#include "gemm.hpp"
 #include "gemv.hpp"
 #include "pack.hpp"
 #include "quant.hpp"
@@ -162,6 +163,29 @@ void launch_generic(const bl::FwdArgs& a, hipStream_t stream)
     hipLaunchKernelGGL((bl::gemv_generic_kernel<FUSED>), dim3(gx, gy), dim3(256), 0, stream, a);
 }
 
+// Many tokens: int8 MFMA GEMM. Needs K % 64 == 0 and 16-byte aligned operands.
+template <int BM, int BN, int WM, int WN, int P>
+void launch_gemm(const bl::FwdArgs& f, hipStream_t stream)
+{
+    bl::GemmArgs a{f.Xq, f.xscale, f.W, f.gamma, f.Y, f.acc, (int)f.M, (int)f.N, f.K};
+    const int64_t tiles = ((f.M + BM - 1) / BM) * ((f.N + BN - 1) / BN);
+    hipLaunchKernelGGL((bl::gemm_mfma_kernel<BM, BN, WM, WN, P>), dim3((unsigned)tiles), dim3(256), 0, stream, a);
+}
+
+bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
+{
+    if (a.M < 16 || a.M > INT32_MAX || (a.K % 64) != 0)
+        return false;
+    if (((a.M + 31) / 32) * ((a.N + 127) / 128) >= INT32_MAX)
+        return false;
+    // Tile shapes from timing the 2B prefill (M = 512, 2048) and 100B (M = 64) shapes.
+    if (a.M >= 1024)
+        launch_gemm<64, 256, 1, 4, 2>(a, stream);
+    else
+        launch_gemm<32, 128, 1, 4, 2>(a, stream);
+    return true;
+}
+
 template <bool FUSED>
 void dispatch_forward(const bl::FwdArgs& a, bool chunk_ok, hipStream_t stream)
 {
@@ -303,7 +327,8 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t M, int64_t
     a.N = N;
     a.K = (int)K;
     const bool chunk_ok = (K % 64) == 0 && aligned(W_packed, 16) && aligned(Xq, 16);
-    dispatch_forward<false>(a, chunk_ok, stream);
+    if (!(chunk_ok && dispatch_gemm(a, stream)))
+        dispatch_forward<false>(a, chunk_ok, stream);
     return launched();
 }
 

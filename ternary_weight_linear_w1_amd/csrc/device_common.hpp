@@ -10,6 +10,8 @@
 
 namespace bl {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr float kFloor = 1e-8f;  // floor of max|x| and of gamma
 constexpr int kWave = 64;
 
@@ -41,16 +43,19 @@ __device__ __forceinline__ float pre_v(float u, int relu2)
     return u;
 }
 
-// Byte-transpose of four dwords: out[f] byte j = in[j] byte f.
+// Byte-transpose of four dwords: out[f] byte j = in[j] byte f. Eight v_perm_b32; a
+// selector byte s picks byte s of the second operand (s < 4) or byte s-4 of the first.
 __device__ __forceinline__ void transpose_bytes(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3,
                                                 uint32_t out[4])
 {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        const int s = 8 * f;
-        out[f] = ((e0 >> s) & 0xffu) | (((e1 >> s) & 0xffu) << 8) | (((e2 >> s) & 0xffu) << 16) |
-                 (((e3 >> s) & 0xffu) << 24);
-    }
+    const uint32_t p0 = __builtin_amdgcn_perm(e1, e0, 0x05010400u);  // e0.0 e1.0 e0.1 e1.1
+    const uint32_t p1 = __builtin_amdgcn_perm(e1, e0, 0x07030602u);  // e0.2 e1.2 e0.3 e1.3
+    const uint32_t p2 = __builtin_amdgcn_perm(e3, e2, 0x05010400u);  // e2.0 e3.0 e2.1 e3.1
+    const uint32_t p3 = __builtin_amdgcn_perm(e3, e2, 0x07030602u);  // e2.2 e3.2 e2.3 e3.3
+    out[0] = __builtin_amdgcn_perm(p2, p0, 0x05040100u);             // e0.0 e1.0 e2.0 e3.0
+    out[1] = __builtin_amdgcn_perm(p2, p0, 0x07060302u);             // e0.1 e1.1 e2.1 e3.1
+    out[2] = __builtin_amdgcn_perm(p3, p1, 0x05040100u);             // e0.2 e1.2 e2.2 e3.2
+    out[3] = __builtin_amdgcn_perm(p3, p1, 0x07060302u);             // e0.3 e1.3 e2.3 e3.3
 }
 
 // ------------------------------------------------------------------------------------

@@ -1,0 +1,258 @@
+// gemm.hpp -- W1.58A8 product for many tokens (prefill, small batches) on the int8
+// matrix cores of gfx950: v_mfma_i32_32x32x32_i8, exact int32 accumulation, fp32 rescale.
+//
+// The work is a dense contraction over K ("BitNet b1.58 深度解析" s.2.3: y = (W_q x_q) *
+// scale), so it runs on MFMA. Operands of one 32x32x32 MFMA: lane l supplies row (l % 32)
+// of A (tokens) and column (l % 32) of B (output features), 16 int8 each for k-slot half
+// l / 32. Which k sits in which slot is free as long as A and B agree; here the slots
+// follow the register unpack of the packed weights:
+//   B  lane half g of k-substep ks holds the packed dword at byte k0/4 + 16g + 4ks of its
+//      row, i.e. codes k0 + 64g + 16ks + 4jj + f (byte jj, field f). (w >> 2f) & 0x03030303
+//      gives the offset codes q + 1 for f = 0..3, which form the four operand dwords.
+//   A  the same 16 activations, byte-transposed once when the tile is staged in LDS
+//      (LDS dword f, byte jj = activation k0 + 16c + 4jj + f).
+// The offset is removed exactly in the epilogue: sum_k (q+1) x - sum_k x.
+//
+// Block: 256 threads = WM x WN waves, block tile BM x BN, K in steps of 128. The
+// activation tile is double-buffered in LDS; global loads run P steps ahead through a
+// ring of VGPR stages while the current step runs on the matrix cores. With WM = 1
+// every wave owns distinct weight columns, so each packed byte is unpacked once per
+// block.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+struct GemmArgs {
+    const int8_t* Xq;     // [M][K]
+    const float* xscale;  // [M]
+    const uint8_t* W;     // [N][K/4]
+    const float* gamma;   // [1]
+    float* Y;             // [M][N]
+    int32_t* acc;         // [M][N] or null
+    int M;
+    int N;
+    int K;
+};
+
+// Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous range of tiles
+// so that the tiles sharing weight columns (consecutive ids, m fastest) share its L2.
+__device__ __forceinline__ int xcd_tile(int bid, int ntiles)
+{
+    constexpr int kXcd = 8;
+    const int per = ntiles / kXcd, rem = ntiles % kXcd;
+    const int x = bid % kXcd, i = bid / kXcd;
+    return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}
+
+// Raw buffer loads: 32-bit offsets from a per-tile base and hardware zero-fill beyond the
+// buffer's size, so rows past M or N need no masks. Descriptor word 3 for gfx9.
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+template <int BM, int BN, int WM, int WN, int P>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
+{
+    static_assert(WM * WN == 4, "four waves per block");
+    constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+    constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
+    static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+    constexpr int BK = 128;
+    constexpr int AST = BK + 16;                 // LDS row stride in bytes (padded)
+    constexpr int AU = BM * (BK / 16) / 256;     // 16-byte activation units per thread per step
+    static_assert(AU >= 1, "block tile too small");
+
+    __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * AST];
+    __shared__ int32_t rsum[BM];
+    __shared__ float csc[BM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int M = a.M, N = a.N, K = a.K;
+    const int KB = K >> 2;
+
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+    const int m0 = (tile % tiles_m) * BM;
+    const int n0 = (tile / tiles_m) * BN;
+
+    if (tid < BM) {
+        const int m = m0 + tid;
+        csc[tid] = m < M ? *a.gamma / a.xscale[m] : 0.0f;
+    }
+
+    const int arows = (M - m0) < BM ? (M - m0) : BM;
+    const int brows = (N - n0) < BN ? (N - n0) : BN;
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.Xq + (int64_t)m0 * K), (short)0, arows * K, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (int64_t)n0 * KB), (short)0, brows * KB, kBufferFlags);
+
+    // Activation unit i of this thread: row (tid + 256 i) / 8, 16-byte column tid % 8.
+    // Weight fragment fn of this lane: row wn*TN + 32 fn + lane % 32, 16 bytes at 16 (lane / 32).
+    int aoff[AU], boff[FN];
+#pragma unroll
+    for (int i = 0; i < AU; ++i)
+        aoff[i] = ((tid + 256 * i) >> 3) * K + 16 * (tid & 7);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        boff[fn] = (wn * TN + fn * 32 + (lane & 31)) * KB + 16 * (lane >> 5);
+    const bool upper_a = (tid & 7) >= 4;      // activation unit in the upper half of a step
+    const bool upper_b = (lane >> 5) != 0;    // weight fragment in the upper half of a step
+
+    // Prefetch ring: the loads for step it + P are issued while step it is computed.
+    u32x4 areg[P][AU];
+    u32x4 breg[P][FN];
+    int32_t rs[AU];
+#pragma unroll
+    for (int i = 0; i < AU; ++i)
+        rs[i] = 0;
+
+    auto load = [&](u32x4 (&ad)[AU], u32x4 (&bd)[FN], int k0) {
+#pragma unroll
+        for (int i = 0; i < AU; ++i)
+            ad[i] = buf_load16(ra, aoff[i], k0);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            bd[fn] = buf_load16(rb, boff[fn], k0 >> 2);
+    };
+    // A step that starts 64 before the end of K covers only its lower half: the upper
+    // half of its loads reaches into the next row and is replaced by zeros.
+    auto store_a = [&](const u32x4 (&src)[AU], int buf, bool half) {
+#pragma unroll
+        for (int i = 0; i < AU; ++i) {
+            const int u = tid + 256 * i;
+            const int r = u >> 3, c = u & 7;
+            u32x4 v = src[i];
+            if (half && upper_a)
+                v = u32x4{0u, 0u, 0u, 0u};
+            uint32_t o[4];
+            transpose_bytes(v[0], v[1], v[2], v[3], o);
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+                rs[i] = __builtin_amdgcn_sdot4((int)o[f], 0x01010101, rs[i], false);
+            *reinterpret_cast<uint4*>(&As[buf][r * AST + 16 * c]) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    };
+
+    v16i C[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                C[fm][fn][r] = 0;
+
+    const int nk = (K + BK - 1) / BK;
+#pragma unroll
+    for (int s = 0; s < P; ++s)
+        if (s < nk)
+            load(areg[s], breg[s], s * BK);
+    store_a(areg[0], 0, K < BK);
+    __syncthreads();
+
+    for (int it0 = 0; it0 < nk; it0 += P) {
+#pragma unroll
+        for (int s = 0; s < P; ++s) {
+            const int it = it0 + s;
+            if (it < nk) {
+                const int buf = it & 1;
+                const bool half = (it + 1) * BK > K;
+                u32x4 bcur[FN];
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    bcur[fn] = breg[s][fn];
+                    if (half && upper_b)
+                        bcur[fn] = u32x4{0u, 0u, 0u, 0u};
+                }
+                if (it + P < nk)
+                    load(areg[s], breg[s], (it + P) * BK);
+                // All operands of the step first (one LDS round trip, unpack on the
+                // VALU), then the 4 * FM * FN matrix instructions back to back.
+                const uint8_t* Ab = As[buf];
+                v4i af[4][FM];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) {
+                        const int r = wm * TM + fm * 32 + (lane & 31);
+                        af[ks][fm] = *reinterpret_cast<const v4i*>(Ab + r * AST + 64 * (lane >> 5) + 16 * ks);
+                    }
+                v4i bf[4][FN];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        const uint32_t w = bcur[fn][ks];
+                        bf[ks][fn][0] = (int)(w & 0x03030303u);
+                        bf[ks][fn][1] = (int)((w >> 2) & 0x03030303u);
+                        bf[ks][fn][2] = (int)((w >> 4) & 0x03030303u);
+                        bf[ks][fn][3] = (int)((w >> 6) & 0x03030303u);
+                    }
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int fm = 0; fm < FM; ++fm)
+                            C[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][fm], bf[ks][fn], C[fm][fn], 0, 0, 0);
+                if (it + 1 < nk)
+                    store_a(areg[(s + 1) % P], buf ^ 1, (it + 2) * BK > K);
+                __syncthreads();
+            }
+        }
+    }
+
+    // Row sums of the activation codes: thread tid holds rows (tid + 256 i) >> 3 for
+    // the column group tid & 7; the eight groups of a row are adjacent lanes.
+#pragma unroll
+    for (int i = 0; i < AU; ++i) {
+        int v = rs[i];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        if ((tid & 7) == 0)
+            rsum[(tid + 256 * i) >> 3] = v;
+    }
+    __syncthreads();
+
+    // C layout of a 32x32 tile: lane l, register r -> column l % 32,
+    // row 8 (r / 4) + 4 (l / 32) + r % 4. Each row's offset and scale are read once.
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = wm * TM + fm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int m = m0 + row;
+            if (m < M) {
+                const int32_t off = rsum[row];
+                const float c = csc[row];
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int n = n0 + wn * TN + fn * 32 + (lane & 31);
+                    if (n < N) {
+                        const int32_t v = C[fm][fn][r] - off;
+                        const int64_t o = (int64_t)m * N + n;
+                        a.Y[o] = (float)v * c;
+                        if (a.acc)
+                            a.acc[o] = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace bl

@@ -25,8 +25,6 @@
 
 namespace bl {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 struct FwdArgs {
     const int8_t* Xq;      // pre-quantized activations [M][K] (unfused)
     const float* xscale;   // [M] (unfused)
