@@ -198,19 +198,23 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
                 if r.get("Counter_Name") != counter:
                     continue
                 rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in rows.items()}
+        return rows
 
     fe = per_kernel(fetch_csv, "FETCH_SIZE")
     wr = per_kernel(write_csv, "WRITE_SIZE")
     gk = [k for k in fe if "gemv_k64_kernel" in k]
-    ck = [k for k in fe if "gemv" not in k and ("copy" in k.lower() or "elementwise" in k.lower())]
+    ck = [k for k in fe if "copy" in k.lower()]
     if len(gk) != 1 or not ck:
         raise SystemExit("could not identify kernels: %s" % list(fe))
-    copyk = max(ck, key=lambda k: fe[k])
-    f_factor = copy_bytes / (fe[copyk] * 1024.0)
-    w_factor = copy_bytes / (wr[copyk] * 1024.0)
-    g_fetch = fe[gk[0]] * 1024.0 * f_factor
-    g_write = wr[gk[0]] * 1024.0 * w_factor
+    # the calibration copy is the largest copy dispatch (copy_bytes read, copy_bytes written)
+    copyk = max(ck, key=lambda k: max(wr.get(k, [0.0])))
+    copy_fetch_kib, copy_write_kib = max(fe[copyk]), max(wr[copyk])
+    f_factor = copy_bytes / (copy_fetch_kib * 1024.0)
+    w_factor = copy_bytes / (copy_write_kib * 1024.0)
+    g_fetch_kib = sum(fe[gk[0]]) / len(fe[gk[0]])
+    g_write_kib = sum(wr[gk[0]]) / len(wr[gk[0]])
+    g_fetch = g_fetch_kib * 1024.0 * f_factor
+    g_write = g_write_kib * 1024.0 * w_factor
     N, K, mode = [(n, k, m) for (nm, n, k, m) in LAYER_2B if nm == DOMINANT][0]
     alg = layer_bytes(N, K, 1, mode)
     with open(out, "w") as f:
@@ -225,9 +229,9 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
         f.write("#   python3 bench.py --summarize-pmc <fetch csv> <write csv>\n")
         f.write("gemv_kernel = %s\n" % gk[0])
         f.write("copy_kernel = %s\n" % copyk)
-        f.write("copy_fetch_kib = %.1f\ncopy_write_kib = %.1f\n" % (fe[copyk], wr[copyk]))
+        f.write("copy_fetch_kib = %.1f\ncopy_write_kib = %.1f\n" % (copy_fetch_kib, copy_write_kib))
         f.write("fetch_scale = %.4f\nwrite_scale = %.4f\n" % (f_factor, w_factor))
-        f.write("gemv_fetch_kib_raw = %.1f\ngemv_write_kib_raw = %.1f\n" % (fe[gk[0]], wr[gk[0]]))
+        f.write("gemv_fetch_kib_raw = %.1f\ngemv_write_kib_raw = %.1f\n" % (g_fetch_kib, g_write_kib))
         f.write("gemv_fetch_bytes = %d\ngemv_write_bytes = %d\n" % (g_fetch, g_write))
         f.write("algorithmic_bytes_per_launch = %d\n" % alg)
         f.write("traffic_bytes_per_launch = %d\n" % (g_fetch + g_write))
