@@ -118,7 +118,7 @@ bool dispatch_mt1(const bl::FwdArgs& a, hipStream_t stream)
         return true;
     }
     if (KC <= 256) { launch_k64<64, 1, 4, 1, FUSED>(a, 2, stream); return true; }
-    if (KC <= 512) { launch_k64<128, 1, 4, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 512) { launch_k64<128, 1, 4, 2, FUSED>(a, 1, stream); return true; }
     if (KC <= 1024) { launch_k64<256, 1, 4, 1, FUSED>(a, 2, stream); return true; }
     return false;
 }
@@ -189,6 +189,9 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
 template <bool FUSED>
 void dispatch_forward(const bl::FwdArgs& a, bool chunk_ok, hipStream_t stream)
 {
+    // 32-bit buffer offsets: a token tile of outputs (4 rows of N floats) must stay
+    // below 2 GiB.
+    chunk_ok = chunk_ok && a.N <= (int64_t(1) << 27);
     if (chunk_ok) {
         if (a.M == 1 && dispatch_mt1<FUSED>(a, stream))
             return;

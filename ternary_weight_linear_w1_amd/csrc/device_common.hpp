@@ -76,9 +76,31 @@ struct RowStats {
     double sumsq;
 };
 
-template <int NT, int KEEP = 0>
-__device__ RowStats row_stats(const float* __restrict__ u, int K, const float* __restrict__ gain, int relu2,
-                              bool want_sumsq, float4* wk = nullptr)
+// Loads of the first KEEP float4 groups of each thread (g = tid + 256 q), issued early
+// so that they are not queued behind other loads; groups past the row give x = 0, g = 1.
+template <int KEEP>
+__device__ __forceinline__ void row_load(const float* __restrict__ u, int K, const float* __restrict__ gain,
+                                         float4 (&xa)[KEEP], float4 (&gb)[KEEP])
+{
+    const int G = K >> 2;
+#pragma unroll
+    for (int q = 0; q < KEEP; ++q) {
+        const int g = (int)threadIdx.x + q * 256;
+        xa[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        gb[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        if (g < G) {
+            xa[q] = reinterpret_cast<const float4*>(u)[g];
+            if (gain)
+                gb[q] = reinterpret_cast<const float4*>(gain)[g];
+        }
+    }
+}
+
+// Statistics from values preloaded by row_load (KEEP > 0, 256 threads) or read here.
+template <int NT, int KEEP>
+__device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const float* __restrict__ gain, int relu2,
+                                  bool want_sumsq, const float4 (&xa)[KEEP > 0 ? KEEP : 1],
+                                  const float4 (&gb)[KEEP > 0 ? KEEP : 1], float4* wk)
 {
     static_assert(NT == 64 || NT == 256, "row_stats supports 64- or 256-thread blocks");
     static_assert(KEEP == 0 || NT == 256, "kept values need one virtual lane per thread");
@@ -106,18 +128,6 @@ __device__ RowStats row_stats(const float* __restrict__ u, int K, const float* _
             return make_float4(wa[0], wa[1], wa[2], wa[3]);
         };
         if constexpr (KEEP > 0) {
-            float4 xa[KEEP], gb[KEEP];
-#pragma unroll
-            for (int q = 0; q < KEEP; ++q) {
-                const int gq = g + q * 256;
-                xa[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                gb[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-                if (gq < G) {
-                    xa[q] = reinterpret_cast<const float4*>(u)[gq];
-                    if (gain)
-                        gb[q] = reinterpret_cast<const float4*>(gain)[gq];
-                }
-            }
 #pragma unroll
             for (int q = 0; q < KEEP; ++q)
                 if (g + q * 256 < G)
@@ -167,6 +177,16 @@ __device__ RowStats row_stats(const float* __restrict__ u, int K, const float* _
     }
     __syncthreads();  // LDS scratch may be reused by the caller
     return RowStats{m, total};
+}
+
+template <int NT, int KEEP = 0>
+__device__ RowStats row_stats(const float* __restrict__ u, int K, const float* __restrict__ gain, int relu2,
+                              bool want_sumsq, float4* wk = nullptr)
+{
+    float4 xa[KEEP > 0 ? KEEP : 1], gb[KEEP > 0 ? KEEP : 1];
+    if constexpr (KEEP > 0)
+        row_load<KEEP>(u, K, gain, xa, gb);
+    return row_stats_pre<NT, KEEP>(u, K, gain, relu2, want_sumsq, xa, gb, wk);
 }
 
 // Scales of one token from its statistics: s' multiplies w to give the codes; the

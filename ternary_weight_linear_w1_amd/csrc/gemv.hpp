@@ -41,46 +41,43 @@ struct FwdArgs {
     int K;
 };
 
-// Loads of one pass: lane j of row group `slot` fetches, for each of its R rows, the
-// chunks j, j+L, ... (CPL of them) as 16-byte non-temporal loads.
-template <int L, int CPL, int R, int RG>
-__device__ __forceinline__ void load_pass(const uint8_t* __restrict__ W, int64_t KB, int KC, int64_t rb, int64_t N,
-                                          int slot, int j, u32x4 (&w)[R][CPL])
+// Codes of float4 group g (elements 4g..4g+3) as one little-endian dword (natural order).
+__device__ __forceinline__ uint32_t group_codes(float4 w, float sp)
 {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int64_t row = rb + slot + (int64_t)r * RG;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = j + i * L;
-            if (row < N && c < KC)
-                w[r][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + row * KB + (int64_t)c * 16));
-            else
-                w[r][i] = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-}
-
-// Activation codes of MT tokens are staged once per block in LDS, in the unpack order:
-// the 16 codes k0..k0+15 of one 16-element unit u (k0 = 16u) are stored as four dwords,
-// dword f holding codes k0 + 4jj + f in byte jj. Unit u lives at LDS bytes 16u..16u+15,
-// so chunk c (units 4c..4c+3) is the 64 bytes at 64c, read with four 16-byte LDS loads.
-// Codes of float4 group g (elements 4g..4g+3) into the LDS unpack order: element
-// k = 64c + 16d + 4jj + f goes to byte 64c + 4(4d + f) + jj.
-__device__ __forceinline__ void put_group_codes(uint8_t* __restrict__ bytes, int g, float4 w, float sp)
-{
-    const int base = 64 * (g >> 4) + 16 * ((g >> 2) & 3) + (g & 3);
-    bytes[base + 0] = (uint8_t)act_code(w.x, sp);
-    bytes[base + 4] = (uint8_t)act_code(w.y, sp);
-    bytes[base + 8] = (uint8_t)act_code(w.z, sp);
-    bytes[base + 12] = (uint8_t)act_code(w.w, sp);
+    return (uint32_t)(act_code(w.x, sp) & 0xff) | ((uint32_t)(act_code(w.y, sp) & 0xff) << 8) |
+           ((uint32_t)(act_code(w.z, sp) & 0xff) << 16) | ((uint32_t)(act_code(w.w, sp) & 0xff) << 24);
 }
 
 constexpr int kKeep = 8;  // float4 groups per thread kept in VGPRs by the fused prologue
 
+// Early loads of token 0 of a tile: the fp32 row (fused) or the int8 codes, issued
+// before the weight loads so that they are not queued behind them.
+constexpr int kPreUnits = 2;  // 16-byte int8 units per thread preloaded (K <= 8192)
+struct Pre {
+    float4 xa[kKeep];
+    float4 gb[kKeep];
+    uint4 q[kPreUnits];
+};
+
+template <bool FUSED>
+__device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre& p)
+{
+    if constexpr (FUSED) {
+        row_load<kKeep>(a.X + tok * (int64_t)a.K, a.K, a.gain, p.xa, p.gb);
+    } else {
+        const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
+        const int units = a.K >> 4;
+#pragma unroll
+        for (int i = 0; i < kPreUnits; ++i) {
+            const int u = (int)threadIdx.x + 256 * i;
+            p.q[i] = u < units ? src[u] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+}
+
 template <int MT, bool FUSED>
 __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt, uint4* __restrict__ lds,
-                                            float (&s)[MT])
+                                            float (&s)[MT], const Pre& pre)
 {
     constexpr int NT = 256;
     const int tid = threadIdx.x;
@@ -99,16 +96,21 @@ __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt
             const float* x = a.X + tok * (int64_t)a.K;
             const bool norm = a.gain != nullptr;
             float4 wk[kKeep];
-            const RowStats st = row_stats<NT, kKeep>(x, a.K, a.gain, a.relu2, norm, wk);
+            RowStats st;
+            if (t == 0) {
+                st = row_stats_pre<NT, kKeep>(x, a.K, a.gain, a.relu2, norm, pre.xa, pre.gb, wk);
+            } else {
+                st = row_stats<NT, kKeep>(x, a.K, a.gain, a.relu2, norm, wk);
+            }
             float sp;
             token_scales(st, a.K, norm, a.eps, sp, s[t]);
-            uint8_t* bytes = reinterpret_cast<uint8_t*>(dst);
+            uint32_t* words = reinterpret_cast<uint32_t*>(dst);
             const int G = a.K >> 2;
 #pragma unroll
             for (int q = 0; q < kKeep; ++q) {
                 const int g = tid + q * NT;
                 if (g < G)
-                    put_group_codes(bytes, g, wk[q], sp);
+                    words[g] = group_codes(wk[q], sp);
             }
             for (int g = tid + kKeep * NT; g < G; g += NT) {
                 const float4 xv = reinterpret_cast<const float4*>(x)[g];
@@ -123,30 +125,59 @@ __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt
                     const float v = pre_v(xa[f], a.relu2);
                     wa[f] = norm ? v * ga[f] : v;
                 }
-                put_group_codes(bytes, g, make_float4(wa[0], wa[1], wa[2], wa[3]), sp);
+                words[g] = group_codes(make_float4(wa[0], wa[1], wa[2], wa[3]), sp);
             }
         } else {
             s[t] = a.xscale[tok];
             const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
-            for (int u = tid; u < units; u += NT) {
-                const uint4 v = src[u];
-                uint32_t o[4];
-                transpose_bytes(v.x, v.y, v.z, v.w, o);
-                dst[u] = make_uint4(o[0], o[1], o[2], o[3]);
+            int u = tid;
+            if (t == 0) {
+#pragma unroll
+                for (int i = 0; i < kPreUnits; ++i, u += NT)
+                    if (u < units)
+                        dst[u] = pre.q[i];
             }
+            for (; u < units; u += NT)
+                dst[u] = src[u];
         }
     }
 }
 
+// Sum over aligned groups of L lanes (every lane of the group gets the sum). Within a
+// row of 16 lanes: DPP quad permutes and the (half) row mirror; across rows: shuffles.
+template <int L>
+__device__ __forceinline__ int group_sum(int v)
+{
+    if constexpr (L >= 2)
+        v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    if constexpr (L >= 4)
+        v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    if constexpr (L >= 8)
+        v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    if constexpr (L >= 16)
+        v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    if constexpr (L >= 32)
+        v += __shfl_xor(v, 16);
+    if constexpr (L >= 64)
+        v += __shfl_xor(v, 32);
+    return v;
+}
+
+constexpr int kBufFlags = 0x00020000;  // buffer descriptor word 3 (gfx9)
+constexpr int kOob = 0x7ffffff0;       // an offset past every buffer: loads give 0, stores drop
+
 // L lanes per row, MT tokens per tile, CPL chunks per lane (16*CPL*MT VGPRs of
-// activation codes, CPL*MT <= 4), R rows per lane per pass: R*CPL 16-byte weight loads
+// activation codes, CPL*MT <= 8), R rows per lane per pass: R*CPL 16-byte weight loads
 // are in flight per lane, and the next pass is requested before the current one is
-// computed.
+// computed. Weights are read and outputs written with raw buffer instructions whose
+// descriptor is rebased per pass; lanes without a valid chunk or row use an offset past
+// the end (hardware zero-fill / dropped store), so the loop has no branches and the
+// outstanding-load counts stay exact.
 template <int L, int MT, int CPL, int R, bool FUSED>
 __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
 {
     constexpr int NT = 256;
-    static_assert(CPL * MT <= 4, "activation codes must fit in 64 VGPRs");
+    static_assert(CPL * MT <= 8, "activation codes must fit in 128 VGPRs");
     constexpr int RG = NT / L;             // row groups per block
     constexpr int RPP = RG * R;            // rows per pass
     constexpr int WPR = L > 64 ? L / 64 : 1;
@@ -156,9 +187,29 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
     const int j = tid % L;
     const int slot = tid / L;
     const int KC = a.K >> 6;
-    const int64_t KB = a.K >> 2;
+    const int KB = a.K >> 2;
+    const int64_t N = a.N;
     const int64_t ntiles = (a.M + MT - 1) / MT;
     const float gamma = *a.gamma;
+
+    int woff[R][CPL];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = j + i * L;
+            woff[r][i] = c < KC ? (slot + r * RG) * KB + c * 16 : kOob;
+        }
+    auto load_pass = [&](int64_t rb, u32x4 (&w)[R][CPL]) {
+        const int64_t rows = rb < N ? ((N - rb) < RPP ? (N - rb) : RPP) : 0;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (rb < N ? rb : 0) * KB), (short)0, (int)(rows * KB), kBufFlags);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                w[r][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, woff[r][i], 0, 2));
+    };
 
     for (int64_t tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
         const int64_t t0 = tile * MT;
@@ -166,13 +217,17 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
         const int64_t pstride = (int64_t)gridDim.x * RPP;
         int64_t rb = (int64_t)blockIdx.x * RPP;
 
-        // Weights of the first pass are requested before the activation prologue.
-        u32x4 cur[R][CPL];
-        load_pass<L, CPL, R, RG>(a.W, KB, KC, rb, a.N, slot, j, cur);
+        // Activations of token 0 first, then the first two passes of weights, then the
+        // prologue arithmetic while the weights are in flight.
+        Pre pre;
+        stage_preload<FUSED>(a, t0, pre);
+        u32x4 cur[R][CPL], nxt[R][CPL];
+        load_pass(rb, cur);
+        load_pass(rb + pstride, nxt);
 
         float s[MT];
         __syncthreads();  // LDS of the previous tile is no longer read
-        stage_codes<MT, FUSED>(a, t0, mt, lds_codes, s);
+        stage_codes<MT, FUSED>(a, t0, mt, lds_codes, s, pre);
         __syncthreads();
 
         uint32_t act[MT][CPL][16];
@@ -190,10 +245,12 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
                     uint4 v = make_uint4(0u, 0u, 0u, 0u);
                     if (c < KC)
                         v = src[4 * c + d];
-                    act[t][i][4 * d + 0] = v.x;
-                    act[t][i][4 * d + 1] = v.y;
-                    act[t][i][4 * d + 2] = v.z;
-                    act[t][i][4 * d + 3] = v.w;
+                    uint32_t o[4];
+                    transpose_bytes(v.x, v.y, v.z, v.w, o);
+                    act[t][i][4 * d + 0] = o[0];
+                    act[t][i][4 * d + 1] = o[1];
+                    act[t][i][4 * d + 2] = o[2];
+                    act[t][i][4 * d + 3] = o[3];
                 }
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
@@ -203,10 +260,14 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
             csc[t] = gamma / s[t];
         }
 
-        for (; rb < a.N; rb += pstride) {
-            u32x4 nxt[R][CPL];
-            load_pass<L, CPL, R, RG>(a.W, KB, KC, rb + pstride, a.N, slot, j, nxt);
+        // Outputs of this token tile: y (and acc when requested; otherwise a zero-size
+        // buffer that drops every store).
+        const __amdgpu_buffer_rsrc_t ry =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.Y + t0 * N), (short)0, (int)(mt * N * 4), kBufFlags);
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            a.acc ? (void*)(a.acc + t0 * N) : (void*)a.Y, (short)0, a.acc ? (int)(mt * N * 4) : 0, kBufFlags);
 
+        auto compute_pass = [&](int64_t pb, const u32x4 (&w)[R][CPL]) {
             int32_t accv[R][MT];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -215,7 +276,7 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
                     accv[r][t] = 0;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
-                    const uint32_t wd[4] = {cur[r][i].x, cur[r][i].y, cur[r][i].z, cur[r][i].w};
+                    const uint32_t wd[4] = {w[r][i].x, w[r][i].y, w[r][i].z, w[r][i].w};
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
 #pragma unroll
@@ -228,14 +289,8 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
                     }
                 }
 #pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    int32_t v = accv[r][t] - xs[t];
-                    constexpr int top = L <= 64 ? L / 2 : 32;
-#pragma unroll
-                    for (int m = top; m >= 1; m >>= 1)
-                        v += __shfl_xor(v, m);
-                    accv[r][t] = v;
-                }
+                for (int t = 0; t < MT; ++t)
+                    accv[r][t] = group_sum<(L < 64 ? L : 64)>(accv[r][t] - xs[t]);
             }
             if constexpr (L > 64) {
                 if ((tid & 63) == 0) {
@@ -246,42 +301,40 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
                             xred[slot][j / 64][r][t] = accv[r][t];
                 }
                 __syncthreads();
-                if (j == 0) {
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                        for (int t = 0; t < MT; ++t) {
-                            int32_t v = 0;
+                    for (int t = 0; t < MT; ++t) {
+                        int32_t v = 0;
 #pragma unroll
-                            for (int w = 0; w < WPR; ++w)
-                                v += xred[slot][w][r][t];
-                            accv[r][t] = v;
-                        }
-                }
+                        for (int wv = 0; wv < WPR; ++wv)
+                            v += xred[slot][wv][r][t];
+                        accv[r][t] = v;
+                    }
                 __syncthreads();
             }
-            if (j == 0) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int64_t row = rb + slot + (int64_t)r * RG;
-                    if (row < a.N) {
+            for (int r = 0; r < R; ++r) {
+                const int64_t row = pb + slot + (int64_t)r * RG;
 #pragma unroll
-                        for (int t = 0; t < MT; ++t) {
-                            if (t < mt) {
-                                const int64_t o = (t0 + t) * a.N + row;
-                                a.Y[o] = (float)accv[r][t] * csc[t];
-                                if (a.acc)
-                                    a.acc[o] = accv[r][t];
-                            }
-                        }
-                    }
+                for (int t = 0; t < MT; ++t) {
+                    const bool mine = j == 0 && row < N && t < mt;
+                    const int off = mine ? (int)((t * N + row) * 4) : kOob;
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, (float)accv[r][t] * csc[t]), ry, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(accv[r][t], ra, off, 0, 0);
                 }
             }
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int i = 0; i < CPL; ++i)
-                    cur[r][i] = nxt[r][i];
+        };
+
+        // Two named buffers in turn (no register copy at the loop edge), so each wait
+        // for weight data sits right before its use; two passes are in flight.
+        for (; rb < N; rb += 2 * pstride) {
+            compute_pass(rb, cur);
+            load_pass(rb + 2 * pstride, cur);
+            if (rb + pstride >= N)
+                break;
+            compute_pass(rb + pstride, nxt);
+            load_pass(rb + 3 * pstride, nxt);
         }
     }
 }
