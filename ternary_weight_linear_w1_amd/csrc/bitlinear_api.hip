@@ -164,12 +164,13 @@ void launch_generic(const bl::FwdArgs& a, hipStream_t stream)
 }
 
 // Many tokens: int8 MFMA GEMM. Needs K % 64 == 0 and 16-byte aligned operands.
-template <int BM, int BN, int WM, int WN, int P>
+template <int BM, int BN, int WM, int WN, int P, int BK>
 void launch_gemm(const bl::FwdArgs& f, hipStream_t stream)
 {
     bl::GemmArgs a{f.Xq, f.xscale, f.W, f.gamma, f.Y, f.acc, (int)f.M, (int)f.N, f.K};
     const int64_t tiles = ((f.M + BM - 1) / BM) * ((f.N + BN - 1) / BN);
-    hipLaunchKernelGGL((bl::gemm_mfma_kernel<BM, BN, WM, WN, P>), dim3((unsigned)tiles), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bl::gemm_mfma_kernel<BM, BN, WM, WN, P, false, BK>), dim3((unsigned)tiles), dim3(256), 0,
+                       stream, a);
 }
 
 bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
@@ -180,9 +181,9 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
         return false;
     // Tile shapes from timing the 2B prefill (M = 512, 2048) and 100B (M = 64) shapes.
     if (a.M >= 1024)
-        launch_gemm<64, 256, 1, 4, 2>(a, stream);
+        launch_gemm<64, 256, 1, 4, 2, 128>(a, stream);
     else
-        launch_gemm<32, 128, 1, 4, 2>(a, stream);
+        launch_gemm<32, 128, 1, 4, 2, 256>(a, stream);
     return true;
 }
 

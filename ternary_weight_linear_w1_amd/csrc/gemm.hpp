@@ -58,16 +58,19 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-template <int BM, int BN, int WM, int WN, int P>
+template <int BM, int BN, int WM, int WN, int P, bool SCHED = false, int BK = 128>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
 {
     static_assert(WM * WN == 4, "four waves per block");
     constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
     constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
     static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-    constexpr int BK = 128;
+    static_assert(BK == 128 || BK == 256, "K step of 128 or 256");
+    constexpr int KS = BK / 32;                  // MFMA k-substeps per step
+    constexpr int BH = BK / 128;                 // 16-byte weight loads per fragment per step
     constexpr int AST = BK + 16;                 // LDS row stride in bytes (padded)
-    constexpr int AU = BM * (BK / 16) / 256;     // 16-byte activation units per thread per step
+    constexpr int UPR = BK / 16;                 // 16-byte activation units per row
+    constexpr int AU = BM * UPR / 256;           // 16-byte activation units per thread per step
     static_assert(AU >= 1, "block tile too small");
 
     __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * AST];
@@ -99,43 +102,45 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
     const __amdgpu_buffer_rsrc_t rb =
         __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (int64_t)n0 * KB), (short)0, brows * KB, kBufferFlags);
 
-    // Activation unit i of this thread: row (tid + 256 i) / 8, 16-byte column tid % 8.
-    // Weight fragment fn of this lane: row wn*TN + 32 fn + lane % 32, 16 bytes at 16 (lane / 32).
+    // Activation unit i of this thread: row (tid + 256 i) / UPR, 16-byte column tid % UPR.
+    // Weight fragment fn of this lane: row wn*TN + 32 fn + lane % 32; for each 128-wide
+    // half h of the step, 16 bytes at 32 h + 16 (lane / 32).
     int aoff[AU], boff[FN];
 #pragma unroll
     for (int i = 0; i < AU; ++i)
-        aoff[i] = ((tid + 256 * i) >> 3) * K + 16 * (tid & 7);
+        aoff[i] = ((tid + 256 * i) / UPR) * K + 16 * (tid % UPR);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
         boff[fn] = (wn * TN + fn * 32 + (lane & 31)) * KB + 16 * (lane >> 5);
-    const bool upper_a = (tid & 7) >= 4;      // activation unit in the upper half of a step
-    const bool upper_b = (lane >> 5) != 0;    // weight fragment in the upper half of a step
+    const int acol = 16 * (tid % UPR);        // k offset of this thread's activation unit
 
     // Prefetch ring: the loads for step it + P are issued while step it is computed.
     u32x4 areg[P][AU];
-    u32x4 breg[P][FN];
+    u32x4 breg[P][FN][BH];
     int32_t rs[AU];
 #pragma unroll
     for (int i = 0; i < AU; ++i)
         rs[i] = 0;
 
-    auto load = [&](u32x4 (&ad)[AU], u32x4 (&bd)[FN], int k0) {
+    auto load = [&](u32x4 (&ad)[AU], u32x4 (&bd)[FN][BH], int k0) {
 #pragma unroll
         for (int i = 0; i < AU; ++i)
             ad[i] = buf_load16(ra, aoff[i], k0);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-            bd[fn] = buf_load16(rb, boff[fn], k0 >> 2);
+#pragma unroll
+            for (int h = 0; h < BH; ++h)
+                bd[fn][h] = buf_load16(rb, boff[fn], (k0 >> 2) + 32 * h);
     };
-    // A step that starts 64 before the end of K covers only its lower half: the upper
-    // half of its loads reaches into the next row and is replaced by zeros.
-    auto store_a = [&](const u32x4 (&src)[AU], int buf, bool half) {
+    // The last step may extend past K (K % BK is a multiple of 64): data loaded from
+    // beyond the row end belongs to the next row and is replaced by zeros.
+    auto store_a = [&](const u32x4 (&src)[AU], int buf, int kvalid) {
 #pragma unroll
         for (int i = 0; i < AU; ++i) {
             const int u = tid + 256 * i;
-            const int r = u >> 3, c = u & 7;
+            const int r = u / UPR, c = u % UPR;
             u32x4 v = src[i];
-            if (half && upper_a)
+            if (acol >= kvalid)
                 v = u32x4{0u, 0u, 0u, 0u};
             uint32_t o[4];
             transpose_bytes(v[0], v[1], v[2], v[3], o);
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
     for (int s = 0; s < P; ++s)
         if (s < nk)
             load(areg[s], breg[s], s * BK);
-    store_a(areg[0], 0, K < BK);
+    store_a(areg[0], 0, K);
     __syncthreads();
 
     for (int it0 = 0; it0 < nk; it0 += P) {
@@ -169,62 +174,75 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
             const int it = it0 + s;
             if (it < nk) {
                 const int buf = it & 1;
-                const bool half = (it + 1) * BK > K;
-                u32x4 bcur[FN];
+                const int kvalid = K - it * BK;   // valid k within this step
+                u32x4 bcur[FN][BH];
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                    bcur[fn] = breg[s][fn];
-                    if (half && upper_b)
-                        bcur[fn] = u32x4{0u, 0u, 0u, 0u};
-                }
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int h = 0; h < BH; ++h) {
+                        bcur[fn][h] = breg[s][fn][h];
+                        if (128 * h + 64 * (lane >> 5) >= kvalid)
+                            bcur[fn][h] = u32x4{0u, 0u, 0u, 0u};
+                    }
                 if (it + P < nk)
                     load(areg[s], breg[s], (it + P) * BK);
                 // All operands of the step first (one LDS round trip, unpack on the
                 // VALU), then the 4 * FM * FN matrix instructions back to back.
                 const uint8_t* Ab = As[buf];
-                v4i af[4][FM];
+                v4i af[KS][FM];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
+                for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                     for (int fm = 0; fm < FM; ++fm) {
                         const int r = wm * TM + fm * 32 + (lane & 31);
-                        af[ks][fm] = *reinterpret_cast<const v4i*>(Ab + r * AST + 64 * (lane >> 5) + 16 * ks);
+                        af[ks][fm] = *reinterpret_cast<const v4i*>(Ab + r * AST + 128 * (ks >> 2) + 64 * (lane >> 5) +
+                                                                   16 * (ks & 3));
                     }
-                v4i bf[4][FN];
+                v4i bf[KS][FN];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
+                for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn) {
-                        const uint32_t w = bcur[fn][ks];
+                        const uint32_t w = bcur[fn][ks >> 2][ks & 3];
                         bf[ks][fn][0] = (int)(w & 0x03030303u);
                         bf[ks][fn][1] = (int)((w >> 2) & 0x03030303u);
                         bf[ks][fn][2] = (int)((w >> 4) & 0x03030303u);
                         bf[ks][fn][3] = (int)((w >> 6) & 0x03030303u);
                     }
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
+                for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                         for (int fm = 0; fm < FM; ++fm)
                             C[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][fm], bf[ks][fn], C[fm][fn], 0, 0, 0);
+                if constexpr (SCHED) {
+                    // Interleave: each matrix instruction is followed by a few VALU
+                    // (unpack) and LDS reads, so they issue while the MFMA executes.
+#pragma unroll
+                    for (int q = 0; q < KS * FM * FN; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, (7 * FN * 4 + 4 * FM * FN) / (4 * FM * FN) + 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                }
                 if (it + 1 < nk)
-                    store_a(areg[(s + 1) % P], buf ^ 1, (it + 2) * BK > K);
+                    store_a(areg[(s + 1) % P], buf ^ 1, K - (it + 1) * BK);
                 __syncthreads();
             }
         }
     }
 
-    // Row sums of the activation codes: thread tid holds rows (tid + 256 i) >> 3 for
-    // the column group tid & 7; the eight groups of a row are adjacent lanes.
+    // Row sums of the activation codes: thread tid holds rows (tid + 256 i) / UPR for
+    // the column group tid % UPR; the UPR groups of a row are adjacent lanes.
 #pragma unroll
     for (int i = 0; i < AU; ++i) {
         int v = rs[i];
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
-        if ((tid & 7) == 0)
-            rsum[(tid + 256 * i) >> 3] = v;
+#pragma unroll
+        for (int m = 1; m < UPR; m <<= 1)
+            v += __shfl_xor(v, m);
+        if ((tid % UPR) == 0)
+            rsum[(tid + 256 * i) / UPR] = v;
     }
     __syncthreads();
 
