@@ -1,0 +1,112 @@
+"""GPU parity at the benchmark's full sizes, through the same entry points and launch
+configurations bench.py times.
+
+Latent weights are drawn on the device (datagen's Philox generators) and copied to the
+host for the oracle, which recomputes gamma over the whole matrix and packs it; packed
+bytes and gamma are compared in full. Outputs are compared in full where the oracle is
+fast enough (M <= 8) and on sampled output rows otherwise (every token, 48 rows spread
+over N including the last).
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import ternary_weight_linear_w1_amd as bl
+from ternary_weight_linear_w1_amd import _build
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+EPS = 1e-5
+
+LAYER_2B = [("qkv", 3840, 2560, "plain"), ("o", 2560, 2560, "norm"), ("up", 6912, 2560, "plain"),
+            ("down", 2560, 6912, "relu2norm")]
+LAYER_100B = [("qkv", 10240, 8192, "plain"), ("o", 8192, 8192, "norm"), ("up", 28672, 8192, "plain"),
+              ("down", 8192, 28672, "relu2norm")]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not _build.up_to_date():
+        _build.build()
+    bl.lib()
+    oracle.lib()
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+
+
+def sample_rows(n, count=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.choice(n, size=min(count, n), replace=False), [0, n - 1]]))
+    return rows
+
+
+def check_matrix(cfg, idx, N, K, mode, M, fused, heavy=False, sampled=False):
+    w = datagen.gg_weights_torch(N, K, datagen.stream_id(cfg, 9, idx, 0), DEV)
+    if heavy:
+        x = datagen.heavy_channel_acts_torch(M, K, datagen.stream_id(cfg, 9, idx, 1), DEV)
+    else:
+        x = datagen.outlier_acts_torch(M, K, datagen.stream_id(cfg, 9, idx, 1), DEV)
+    gain = datagen.gains_torch(K, datagen.stream_id(cfg, 9, idx, 2), DEV) if "norm" in mode else None
+    relu2 = mode == "relu2norm"
+    packed, gamma = bl.bitlinear_pack_weights(w)
+    if fused:
+        y = bl.bitlinear_forward_f32(x, packed, gamma, gain, EPS, relu2)
+        acc = None
+    else:
+        xq, s = bl.bitlinear_quantize_act(x, gain, EPS, relu2)
+        y, acc = bl.bitlinear_forward(xq, s, packed, gamma, acc=True)
+    torch.cuda.synchronize()
+    wh = w.cpu().numpy()
+    xh = x.cpu().numpy()
+    gh = None if gain is None else gain.cpu().numpy()
+    del w
+    # full weight-side parity
+    opacked, ogamma, _ = oracle.pack_weights(wh)
+    assert float(gamma.cpu()[0]) == float(ogamma)
+    assert np.array_equal(packed.cpu().numpy(), opacked)
+    # activation side
+    if gh is None and not relu2:
+        oxq, os_ = oracle.quantize_act(xh)
+    else:
+        oxq, os_ = oracle.quantize_act_norm(xh, gh, EPS, relu2)
+    rows = sample_rows(N, seed=idx) if sampled else np.arange(N)
+    q_rows = oracle.weight_codes(wh[rows], ogamma)
+    oacc, oy = oracle.forward(oxq, os_, q_rows, ogamma)
+    yh = y.cpu().numpy()[:, rows]
+    if acc is not None:
+        assert np.array_equal(acc.cpu().numpy()[:, rows], oacc)
+    if gh is None:
+        assert np.array_equal(yh.view(np.int32), oy.view(np.int32))
+    else:
+        err = np.abs(yh.astype(np.float64) - oy.astype(np.float64))
+        assert (err <= 1e-6 * np.abs(oy.astype(np.float64))).all()
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("i", range(4))
+def test_2b_layer_decode(M, i):
+    name, N, K, mode = LAYER_2B[i]
+    check_matrix(2, i + 10 * M, N, K, mode, M, fused=(M == 1))
+    if M > 1:
+        check_matrix(2, i + 10 * M + 100, N, K, mode, M, fused=True)
+
+
+@pytest.mark.parametrize("M", [512, 2048])
+@pytest.mark.parametrize("i", range(4))
+def test_2b_prefill(M, i):
+    name, N, K, mode = LAYER_2B[i]
+    check_matrix(4, i + M, N, K, "plain", M, fused=False, heavy=True, sampled=True)
+
+
+@pytest.mark.parametrize("i", range(4))
+def test_100b_decode_m1(i):
+    name, N, K, mode = LAYER_100B[i]
+    check_matrix(5, i, N, K, mode, 1, fused=True)
+
+
+@pytest.mark.parametrize("i", range(4))
+def test_100b_small_batch_m64(i):
+    name, N, K, mode = LAYER_100B[i]
+    check_matrix(5, i + 64, N, K, mode, 64, fused=False, sampled=True)
