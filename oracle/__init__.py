@@ -124,16 +124,24 @@ def quantize_act(x: np.ndarray):
     return xq, s
 
 
-def quantize_act_norm(u: np.ndarray, gain, eps: float, relu2: bool):
-    """Fused [ReLU^2] -> RMSNorm(gain, eps) -> absmax quant; gain None = no norm."""
+def quantize_act_norm(u: np.ndarray, gain, eps: float, relu2):
+    """Fused [activation] -> RMSNorm(gain, eps) -> absmax quant; gain None = no norm.
+
+    relu2: 0/False = none, 1/True = squared ReLU, 2 = gated squared ReLU (u holds
+    [gate | up], 2K values per token)."""
+    act = int(relu2)
     u = _c(u, np.float32)
     m, k = u.shape
+    if act == 2:
+        if k % 2:
+            raise ValueError("gated input needs an even row length")
+        k //= 2
     xq = np.empty((m, k), dtype=np.int8)
     s = np.empty(m, dtype=np.float32)
     work = np.empty(k, dtype=np.float32)
     g = None if gain is None else _c(gain, np.float32)
     lib().ora_quantize_act_norm(_ptr(u), m, k, None if g is None else _ptr(g), np.float32(eps),
-                                1 if relu2 else 0, _ptr(xq), _ptr(s), _ptr(work))
+                                act, _ptr(xq), _ptr(s), _ptr(work))
     return xq, s
 
 
@@ -154,8 +162,9 @@ def forward(xq: np.ndarray, s: np.ndarray, q: np.ndarray, gamma):
     return acc, y
 
 
-def bitlinear(x: np.ndarray, w: np.ndarray, gain=None, eps: float = 1e-5, relu2: bool = False):
-    """Whole path on latent inputs: quantize W and x, accumulate, rescale."""
+def bitlinear(x: np.ndarray, w: np.ndarray, gain=None, eps: float = 1e-5, relu2=False):
+    """Whole path on latent inputs: quantize W and x, accumulate, rescale.
+    relu2 as in quantize_act_norm (0, 1, or 2 = gated with x = [gate | up])."""
     packed, gamma, q = pack_weights(w)
     if gain is None and not relu2:
         xq, s = quantize_act(x)

@@ -169,12 +169,16 @@ void ora_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* s
 }
 
 /* ---------------------------------------------------------------------------------
- * O5  subln input: [ReLU^2] -> RMSNorm(gain, eps) -> per-token absmax int8
+ * O5  subln input: [activation] -> RMSNorm(gain, eps) -> per-token absmax int8
  *     (subln: [P1] s.1 "归一化方法", [P3], [P4] s.2, no formula printed; RMSNorm
  *     layers before attention and FFN: [P5] s.2.4; squared ReLU in the FFN: [P1] s.2
- *     "特殊设计"; no bias anywhere: [P1] s.2 "偏置移除").
+ *     "特殊设计"; a gate projection next to the up projection: [P5] s.2.4; no bias
+ *     anywhere: [P1] s.2 "偏置移除").
  *
- *     v_k  = relu2 ? fl(max(u_k,0) * max(u_k,0)) : u_k
+ *     act = 0:  v_k = u_k                                   (row of K values)
+ *     act = 1:  v_k = fl(p * p),        p = max(u_k, 0)     (row of K values)
+ *     act = 2:  v_k = fl(fl(p * p) * up_k), p = max(gate_k, 0)
+ *               (row of 2K values: gate_0..gate_{K-1}, up_0..up_{K-1})
  *     w_k  = fl(v_k * g_k)
  *     RMSNorm output is r * w with r = 1 / sqrt(mean(v^2) + eps), one positive number
  *     per token. Absmax quantization is invariant to a positive per-token factor:
@@ -183,20 +187,23 @@ void ora_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* s
  *         s'   = 127 / max(max_k |w_k|, 1e-8),   xq = clip(rint(w * s'), -128, 127),
  *     and r survives only in the stored scale of the normalized activation,
  *         s_t  = s' / r = s' * sqrt(mean_k v_k^2 + eps)      (binary64, then to fp32).
- *     With gain == NULL no normalization is applied (only the optional ReLU^2).
+ *     With gain == NULL no normalization is applied (only the activation).
  * ------------------------------------------------------------------------------- */
 void ora_quantize_act_norm(const float* u, int64_t M, int64_t K, const float* gain, float eps,
-                           int relu2, int8_t* xq, float* scale, float* work /* K floats */)
+                           int act, int8_t* xq, float* scale, float* work /* K floats */)
 {
+    const int64_t stride = act == 2 ? 2 * K : K;
     for (int64_t t = 0; t < M; ++t) {
-        const float* row = u + t * K;
+        const float* row = u + t * stride;
         double sumsq = 0.0;
         float m = 0.0f;
         for (int64_t k = 0; k < K; ++k) {
             float v = row[k];
-            if (relu2) {
+            if (act == 1 || act == 2) {
                 float p = v > 0.0f ? v : 0.0f;
                 v = p * p;
+                if (act == 2)
+                    v = v * row[K + k];
             }
             sumsq += (double)v * (double)v;
             float w = gain ? v * gain[k] : v;

@@ -314,3 +314,38 @@ def test_forward_bound(ora):
     r = ora.bitlinear(x, w)
     nnz = (r["q"] != 0).sum(axis=1)
     assert (np.abs(r["acc"]) <= 127 * nnz[None, :]).all()
+
+
+# ----------------------------------------------------------------------------- gated FFN input
+
+def test_gated_golden(ora, golden):
+    g = golden["gated_relu2"]
+    xq, s = ora.quantize_act_norm(np.array(g["U"], np.float32), None, 1e-5, 2)
+    assert xq.tolist() == g["codes"]
+    assert s[0] == F32(127.0) / F32(9.0)
+
+
+def test_gated_reduces_to_relu2_when_up_is_one(ora):
+    """relu(gate)^2 * 1 is relu(gate)^2: the gated mode with up = 1 equals mode 1."""
+    gate = datagen.outlier_acts(6, 2560, 51)
+    g = datagen.gains(2560, 52)
+    u = np.concatenate([gate, np.ones_like(gate)], axis=1)
+    xq1, s1 = ora.quantize_act_norm(gate, g, 1e-5, True)
+    xq2, s2 = ora.quantize_act_norm(u, g, 1e-5, 2)
+    assert (xq1 == xq2).all() and (s1 == s2).all()
+
+
+def test_gated_codes_are_plain_codes_of_the_product(ora):
+    """Codes of the gated input equal plain absmax codes of fl(fl(p^2) * up) * g."""
+    gate = datagen.outlier_acts(5, 6912, 53)
+    up = datagen.outlier_acts(5, 6912, 54)
+    g = datagen.gains(6912, 55)
+    xq, s = ora.quantize_act_norm(np.concatenate([gate, up], axis=1), g, 1e-5, 2)
+    p = np.maximum(gate, 0).astype(np.float32)
+    v = ((p * p).astype(np.float32) * up).astype(np.float32)
+    xq_plain, _ = ora.quantize_act((v * g).astype(np.float32))
+    assert (xq == xq_plain).all()
+    ms = (v.astype(np.float64) ** 2).mean(axis=1)
+    sp = F32(127.0) / np.maximum(np.abs((v * g).astype(np.float32)).max(axis=1), F32(1e-8))
+    ref = sp.astype(np.float64) * np.sqrt(ms + float(F32(1e-5)))
+    assert np.allclose(s.astype(np.float64), ref, rtol=2e-7, atol=0)
