@@ -80,27 +80,31 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* W_pack
 /*
  * Per-token absmax int8 activation quantization, with an optional fused subln input.
  *
- * Plain (gain == NULL, relu2 == 0): for token t, m = max_k |x_tk|,
+ * Plain (gain == NULL, act == 0): for token t, m = max_k |x_tk|,
  * s_t = 127 / max(m, 1e-8) (fp32 division), xq_tk = clip(round_half_even(x_tk s_t),
  * -128, 127) ("BitNet b1.58 深度解析" s.2.2; per token: "微软AI大模型炸场" s.1,
  * "20亿参数仅0.4GB" s.2).
  *
  * Fused subln input (squared ReLU: "微软AI大模型炸场" s.2 "特殊设计"; subln RMSNorm:
- * same page s.1, RMSNorm layers in "BitNet b1.58 深度解析" s.2.4):
- *   v = relu2 ? max(u,0)^2 : u   (fp32);   w = v * gain (fp32) when gain != NULL.
+ * same page s.1, RMSNorm layers in "BitNet b1.58 深度解析" s.2.4; gate and up
+ * projections of the FFN: "BitNet b1.58 深度解析" s.2.4):
+ *   act 0: v = u;   act 1: v = max(u,0)^2;   act 2: v = max(g,0)^2 * p   (all fp32),
+ * where for act 2 each token row holds 2K values, the gate g = row[0..K) followed by
+ * the up projection p = row[K..2K);   w = v * gain (fp32) when gain != NULL.
  * The RMSNorm output r*w, r = 1/sqrt(mean(v^2) + eps), differs from w by a positive
  * per-token factor, which absmax quantization divides out; the codes are therefore
  * those of w, with s' = 127 / max(max|w|, 1e-8), and the stored scale is that of the
  * normalized activation, s_t = s' * sqrt(mean(v^2) + eps) (binary64, rounded to fp32).
- * relu2 != 0 with gain == NULL applies only the squared ReLU.
+ * act != 0 with gain == NULL applies only the activation.
  *
- *   X        fp32 [M][K], 16-byte aligned
+ *   X        fp32 [M][K] (act 0, 1) or [M][2K] (act 2), 16-byte aligned
+ *   act      0, 1 or 2; any other value is BITLINEAR_ERR_SHAPE
  *   gain     fp32 [K] or NULL (no RMSNorm); eps is used only when gain != NULL
  *   Xq       int8 [M][K] (written), 4-byte aligned
  *   x_scale  fp32 [M] (written): s_t, the multiplier; dequantization is xq / s_t
  */
 int bitlinear_quantize_act(const float* X, int64_t M, int64_t K, const float* gain, float eps,
-                           int relu2, int8_t* Xq, float* x_scale, hipStream_t stream);
+                           int act, int8_t* Xq, float* x_scale, hipStream_t stream);
 
 /*
  * The W1.58A8 product ("20亿参数仅0.4GB" s.2 BitLinear; custom W1.58A8 matmul kernel in
@@ -122,10 +126,10 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t M, int64_t
 
 /*
  * Fused input quantization and product in one launch: bit for bit the result of
- * bitlinear_quantize_act(X, M, K, gain, eps, relu2, ...) followed by bitlinear_forward,
+ * bitlinear_quantize_act(X, M, K, gain, eps, act, ...) followed by bitlinear_forward,
  * without the int8 round trip through memory. Arguments as in those two calls.
  */
-int bitlinear_forward_f32(const float* X, int64_t M, int64_t K, const float* gain, float eps, int relu2,
+int bitlinear_forward_f32(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
                           const uint8_t* W_packed, const float* gamma, int64_t N, float* Y,
                           hipStream_t stream);
 

@@ -118,19 +118,31 @@ def bitlinear_pack_weights(W, packed=None, gamma=None, workspace=None, stream=No
     return packed, gamma
 
 
-def bitlinear_quantize_act(X, gain=None, eps: float = 1e-5, relu2: bool = False, xq=None, scale=None,
-                           stream=None):
-    """fp32 activations [M][K] -> (int8 codes [M][K], per-token scale fp32 [M])."""
+def _act_mode(act, X):
+    """Activation mode (0 none, 1 squared ReLU, 2 gated: X rows are [gate | up]) and K."""
+    act = int(act)
+    if act not in (0, 1, 2):
+        raise ValueError("act must be 0, 1 or 2")
+    M, K = X.shape
+    if act == 2:
+        if K % 2:
+            raise ValueError("gated input needs rows of 2K values")
+        K //= 2
+    return act, M, K
+
+
+def bitlinear_quantize_act(X, gain=None, eps: float = 1e-5, act=0, xq=None, scale=None, stream=None):
+    """fp32 activations [M][K] ([M][2K] when act == 2) -> (int8 codes [M][K], scale fp32 [M])."""
     import torch
     _need(X, torch.float32, "X", 2)
-    M, K = X.shape
+    act, M, K = _act_mode(act, X)
     if gain is not None:
         _need(gain, torch.float32, "gain", 1)
     if xq is None:
         xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
     if scale is None:
         scale = torch.empty((M,), dtype=torch.float32, device=X.device)
-    _check(lib().bitlinear_quantize_act(_ptr(X), M, K, _ptr(gain), float(eps), 1 if relu2 else 0, _ptr(xq),
+    _check(lib().bitlinear_quantize_act(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(xq),
                                         _ptr(scale), _stream(stream)), "bitlinear_quantize_act")
     return xq, scale
 
@@ -156,21 +168,20 @@ def bitlinear_forward(Xq, x_scale, W_packed, gamma, y=None, acc=None, stream=Non
     return (y, acc) if isinstance(acc, torch.Tensor) else y
 
 
-def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, relu2: bool = False, y=None,
-                          stream=None):
-    """Fused quantize + product from fp32 activations [M][K] -> fp32 y [M][N]."""
+def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=0, y=None, stream=None):
+    """Fused quantize + product from fp32 activations [M][K] ([M][2K] when act == 2) -> fp32 y [M][N]."""
     import torch
     _need(X, torch.float32, "X", 2)
     _need(W_packed, torch.uint8, "W_packed", 2)
     _need(gamma, torch.float32, "gamma", 1)
     if gain is not None:
         _need(gain, torch.float32, "gain", 1)
-    M, K = X.shape
+    act, M, K = _act_mode(act, X)
     N = W_packed.shape[0]
     if W_packed.shape[1] * 4 != K:
         raise ValueError("W_packed must have K/4 columns")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=X.device)
-    _check(lib().bitlinear_forward_f32(_ptr(X), M, K, _ptr(gain), float(eps), 1 if relu2 else 0, _ptr(W_packed),
+    _check(lib().bitlinear_forward_f32(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(W_packed),
                                        _ptr(gamma), N, _ptr(y), _stream(stream)), "bitlinear_forward_f32")
     return y

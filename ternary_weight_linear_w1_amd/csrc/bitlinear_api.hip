@@ -277,7 +277,7 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* W_pack
     return launched();
 }
 
-int bitlinear_quantize_act(const float* X, int64_t M, int64_t K, const float* gain, float eps, int relu2,
+int bitlinear_quantize_act(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
                            int8_t* Xq, float* x_scale, hipStream_t stream)
 {
     if (!X || !Xq || !x_scale)
@@ -285,12 +285,15 @@ int bitlinear_quantize_act(const float* X, int64_t M, int64_t K, const float* ga
     int st = check_mk(M, K);
     if (st != BITLINEAR_OK)
         return st;
+    if (act < 0 || act > 2 || (act == 2 && M > kMaxElems / (2 * K)))
+        return BITLINEAR_ERR_SHAPE;
     if (!aligned(X, 16) || !aligned(Xq, 4) || !aligned(x_scale, 4) || (gain && !aligned(gain, 16)))
         return BITLINEAR_ERR_ALIGN;
-    if (overlap(Xq, M * K, X, M * K * 4) || overlap(x_scale, M * 4, X, M * K * 4) ||
+    const int64_t xbytes = M * K * 4 * (act == 2 ? 2 : 1);
+    if (overlap(Xq, M * K, X, xbytes) || overlap(x_scale, M * 4, X, xbytes) ||
         overlap(Xq, M * K, gain, K * 4) || overlap(x_scale, M * 4, gain, K * 4) || overlap(Xq, M * K, x_scale, M * 4))
         return BITLINEAR_ERR_ALIAS;
-    bl::QuantArgs a{X, gain, Xq, x_scale, M, (int)K, eps, relu2 ? 1 : 0};
+    bl::QuantArgs a{X, gain, Xq, x_scale, M, (int)K, eps, act};
     const int64_t max_blocks = int64_t(cu_count()) * 64;
     hipLaunchKernelGGL(bl::quantize_act_kernel, dim3((unsigned)(M < max_blocks ? M : max_blocks)), dim3(256), 0,
                        stream, a);
@@ -336,7 +339,7 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t M, int64_t
     return launched();
 }
 
-int bitlinear_forward_f32(const float* X, int64_t M, int64_t K, const float* gain, float eps, int relu2,
+int bitlinear_forward_f32(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
                           const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, hipStream_t stream)
 {
     if (!X || !W_packed || !gamma || !Y)
@@ -346,13 +349,13 @@ int bitlinear_forward_f32(const float* X, int64_t M, int64_t K, const float* gai
         return st;
     if ((st = check_nk(N, K)) != BITLINEAR_OK)
         return st;
-    if (M > kMaxElems / N)
+    if (M > kMaxElems / N || act < 0 || act > 2 || (act == 2 && M > kMaxElems / (2 * K)))
         return BITLINEAR_ERR_SHAPE;
     if (!aligned(X, 16) || (gain && !aligned(gain, 16)) || !aligned(gamma, 4) || !aligned(Y, 4))
         return BITLINEAR_ERR_ALIGN;
     const int64_t ybytes = M * N * 4;
     const void* ins[4] = {X, gain, W_packed, gamma};
-    const int64_t insz[4] = {M * K * 4, K * 4, N * (K / 4), 4};
+    const int64_t insz[4] = {M * K * 4 * (act == 2 ? 2 : 1), K * 4, N * (K / 4), 4};
     for (int i = 0; i < 4; ++i)
         if (overlap(Y, ybytes, ins[i], insz[i]))
             return BITLINEAR_ERR_ALIAS;
@@ -360,7 +363,7 @@ int bitlinear_forward_f32(const float* X, int64_t M, int64_t K, const float* gai
     a.X = X;
     a.gain = gain;
     a.eps = eps;
-    a.relu2 = relu2 ? 1 : 0;
+    a.act = act;
     a.W = W_packed;
     a.gamma = gamma;
     a.Y = Y;

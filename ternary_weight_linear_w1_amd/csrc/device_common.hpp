@@ -33,14 +33,24 @@ __device__ __forceinline__ int act_code(float v, float s)
     return (int)r;
 }
 
-// Elementwise part of the subln input: squared ReLU (optional), then the gain.
-__device__ __forceinline__ float pre_v(float u, int relu2)
+// Elementwise activation of the subln input: act 0 = identity, 1 = squared ReLU,
+// 2 = squared ReLU of the gate times the up value (gated FFN; `up` is the matching
+// element of the second half of the row).
+__device__ __forceinline__ float pre_v(float u, int act)
 {
-    if (relu2) {
+    if (act) {
         float p = u > 0.0f ? u : 0.0f;
         return p * p;
     }
     return u;
+}
+
+__device__ __forceinline__ float act_v(float u, float up, int act)
+{
+    float v = pre_v(u, act);
+    if (act == 2)
+        v = v * up;
+    return v;
 }
 
 // Byte-transpose of four dwords: out[f] byte j = in[j] byte f. Eight v_perm_b32; a
@@ -59,10 +69,10 @@ __device__ __forceinline__ void transpose_bytes(uint32_t e0, uint32_t e1, uint32
 }
 
 // ------------------------------------------------------------------------------------
-// Per-token statistics of the (optional ReLU^2 + gain) input, shared by the standalone
+// Per-token statistics of the (activation + gain) input, shared by the standalone
 // quantizer and the fused GEMV prologue so that both produce the same bits.
 //
-//   m     = max_k |w_k|,  w_k = pre_v(u_k) * gain_k   (order-free)
+//   m     = max_k |w_k|,  w_k = act_v(u_k, up_k) * gain_k   (order-free)
 //   sumsq = sum_k v_k^2 in binary64 over 256 virtual lanes: virtual lane l adds the
 //           float4 groups g = l, l+256, l+512, ... in increasing order (components in
 //           order), then the 256 lane sums are combined as a pairwise tree in lane
@@ -80,7 +90,7 @@ struct RowStats {
 // so that they are not queued behind other loads; groups past the row give x = 0, g = 1.
 template <int KEEP>
 __device__ __forceinline__ void row_load(const float* __restrict__ u, int K, const float* __restrict__ gain,
-                                         float4 (&xa)[KEEP], float4 (&gb)[KEEP])
+                                         const float* __restrict__ up, float4 (&xa)[KEEP], float4 (&gb)[KEEP])
 {
     const int G = K >> 2;
 #pragma unroll
@@ -90,17 +100,19 @@ __device__ __forceinline__ void row_load(const float* __restrict__ u, int K, con
         gb[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
         if (g < G) {
             xa[q] = reinterpret_cast<const float4*>(u)[g];
-            if (gain)
-                gb[q] = reinterpret_cast<const float4*>(gain)[g];
+            const float* second = up ? up : gain;
+            if (second)
+                gb[q] = reinterpret_cast<const float4*>(second)[g];
         }
     }
 }
 
 // Statistics from values preloaded by row_load (KEEP > 0, 256 threads) or read here.
 template <int NT, int KEEP>
-__device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const float* __restrict__ gain, int relu2,
-                                  bool want_sumsq, const float4 (&xa)[KEEP > 0 ? KEEP : 1],
-                                  const float4 (&gb)[KEEP > 0 ? KEEP : 1], float4* wk)
+__device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const float* __restrict__ gain, int act,
+                                  bool want_sumsq, const float* __restrict__ up,
+                                  const float4 (&xa)[KEEP > 0 ? KEEP : 1], const float4 (&gb)[KEEP > 0 ? KEEP : 1],
+                                  float4* wk)
 {
     static_assert(NT == 64 || NT == 256, "row_stats supports 64- or 256-thread blocks");
     static_assert(KEEP == 0 || NT == 256, "kept values need one virtual lane per thread");
@@ -113,13 +125,14 @@ __device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const floa
     for (int i = 0; i < V; ++i) {
         double s = 0.0;
         int g = tid + i * NT;
-        auto visit = [&](float4 a, float4 gv) -> float4 {
+        auto visit = [&](float4 a, float4 gv, float4 uv) -> float4 {
             const float va[4] = {a.x, a.y, a.z, a.w};
             const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
+            const float ub[4] = {uv.x, uv.y, uv.z, uv.w};
             float wa[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float v = pre_v(va[c], relu2);
+                const float v = act_v(va[c], ub[c], act);
                 if (want_sumsq)
                     s += (double)v * (double)v;
                 wa[c] = gain ? v * ga[c] : v;
@@ -129,17 +142,31 @@ __device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const floa
         };
         if constexpr (KEEP > 0) {
 #pragma unroll
-            for (int q = 0; q < KEEP; ++q)
-                if (g + q * 256 < G)
-                    wk[q] = visit(xa[q], gb[q]);
+            for (int q = 0; q < KEEP; ++q) {
+                if (g + q * 256 < G) {
+                    // gb holds the up values when gated (the gain, a small shared vector, is
+                    // then read here), else the gain
+                    float4 gv = gb[q];
+                    float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                    if (up) {
+                        uv = gb[q];
+                        gv = gain ? reinterpret_cast<const float4*>(gain)[g + q * 256]
+                                  : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                    }
+                    wk[q] = visit(xa[q], gv, uv);
+                }
+            }
             g += KEEP * 256;
         }
         for (; g < G; g += 256) {
             const float4 a = reinterpret_cast<const float4*>(u)[g];
             float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
             if (gain)
                 gv = reinterpret_cast<const float4*>(gain)[g];
-            visit(a, gv);
+            if (up)
+                uv = reinterpret_cast<const float4*>(up)[g];
+            visit(a, gv, uv);
         }
         part[i] = s;
     }
@@ -180,13 +207,13 @@ __device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const floa
 }
 
 template <int NT, int KEEP = 0>
-__device__ RowStats row_stats(const float* __restrict__ u, int K, const float* __restrict__ gain, int relu2,
-                              bool want_sumsq, float4* wk = nullptr)
+__device__ RowStats row_stats(const float* __restrict__ u, int K, const float* __restrict__ gain, int act,
+                              bool want_sumsq, const float* __restrict__ up, float4* wk = nullptr)
 {
     float4 xa[KEEP > 0 ? KEEP : 1], gb[KEEP > 0 ? KEEP : 1];
     if constexpr (KEEP > 0)
-        row_load<KEEP>(u, K, gain, xa, gb);
-    return row_stats_pre<NT, KEEP>(u, K, gain, relu2, want_sumsq, xa, gb, wk);
+        row_load<KEEP>(u, K, gain, up, xa, gb);
+    return row_stats_pre<NT, KEEP>(u, K, gain, act, want_sumsq, up, xa, gb, wk);
 }
 
 // Scales of one token from its statistics: s' multiplies w to give the codes; the

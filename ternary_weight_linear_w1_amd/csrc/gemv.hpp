@@ -28,10 +28,10 @@ namespace bl {
 struct FwdArgs {
     const int8_t* Xq;      // pre-quantized activations [M][K] (unfused)
     const float* xscale;   // [M] (unfused)
-    const float* X;        // fp32 activations [M][K] (fused)
+    const float* X;        // fp32 activations [M][K], [M][2K] when act == 2 (fused)
     const float* gain;     // [K] or null (fused)
     float eps;             // (fused)
-    int relu2;             // (fused)
+    int act;               // activation (fused): 0 identity, 1 squared ReLU, 2 gated
     const uint8_t* W;      // packed [N][K/4]
     const float* gamma;    // [1]
     float* Y;              // [M][N]
@@ -55,15 +55,21 @@ constexpr int kKeep = 8;  // float4 groups per thread kept in VGPRs by the fused
 constexpr int kPreUnits = 2;  // 16-byte int8 units per thread preloaded (K <= 8192)
 struct Pre {
     float4 xa[kKeep];
-    float4 gb[kKeep];
+    float4 gb[kKeep];      // gain, or the up values when gated
     uint4 q[kPreUnits];
 };
+
+__device__ __forceinline__ int64_t x_stride(const FwdArgs& a)
+{
+    return a.act == 2 ? 2 * (int64_t)a.K : (int64_t)a.K;
+}
 
 template <bool FUSED>
 __device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre& p)
 {
     if constexpr (FUSED) {
-        row_load<kKeep>(a.X + tok * (int64_t)a.K, a.K, a.gain, p.xa, p.gb);
+        const float* x = a.X + tok * x_stride(a);
+        row_load<kKeep>(x, a.K, a.gain, a.act == 2 ? x + a.K : nullptr, p.xa, p.gb);
     } else {
         const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
         const int units = a.K >> 4;
@@ -93,14 +99,15 @@ __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt
         }
         const int64_t tok = t0 + t;
         if constexpr (FUSED) {
-            const float* x = a.X + tok * (int64_t)a.K;
+            const float* x = a.X + tok * x_stride(a);
+            const float* up = a.act == 2 ? x + a.K : nullptr;
             const bool norm = a.gain != nullptr;
             float4 wk[kKeep];
             RowStats st;
             if (t == 0) {
-                st = row_stats_pre<NT, kKeep>(x, a.K, a.gain, a.relu2, norm, pre.xa, pre.gb, wk);
+                st = row_stats_pre<NT, kKeep>(x, a.K, a.gain, a.act, norm, up, pre.xa, pre.gb, wk);
             } else {
-                st = row_stats<NT, kKeep>(x, a.K, a.gain, a.relu2, norm, wk);
+                st = row_stats<NT, kKeep>(x, a.K, a.gain, a.act, norm, up, wk);
             }
             float sp;
             token_scales(st, a.K, norm, a.eps, sp, s[t]);
@@ -115,14 +122,18 @@ __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt
             for (int g = tid + kKeep * NT; g < G; g += NT) {
                 const float4 xv = reinterpret_cast<const float4*>(x)[g];
                 float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
                 if (norm)
                     gv = reinterpret_cast<const float4*>(a.gain)[g];
+                if (up)
+                    uv = reinterpret_cast<const float4*>(up)[g];
                 const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
                 const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
+                const float ub[4] = {uv.x, uv.y, uv.z, uv.w};
                 float wa[4];
 #pragma unroll
                 for (int f = 0; f < 4; ++f) {
-                    const float v = pre_v(xa[f], a.relu2);
+                    const float v = act_v(xa[f], ub[f], a.act);
                     wa[f] = norm ? v * ga[f] : v;
                 }
                 words[g] = group_codes(make_float4(wa[0], wa[1], wa[2], wa[3]), sp);
@@ -361,7 +372,8 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(FwdArgs a)
             sp[t] = 1.0f;
             if (t < mt) {
                 if constexpr (FUSED) {
-                    const RowStats st = row_stats<256>(a.X + (t0 + t) * (int64_t)a.K, a.K, a.gain, a.relu2, norm);
+                    const float* x = a.X + (t0 + t) * x_stride(a);
+                    const RowStats st = row_stats<256>(x, a.K, a.gain, a.act, norm, a.act == 2 ? x + a.K : nullptr);
                     token_scales(st, a.K, norm, a.eps, sp[t], s);
                 } else {
                     s = a.xscale[t0 + t];
@@ -384,7 +396,8 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(FwdArgs a)
                             if (t < mt) {
                                 int xv;
                                 if constexpr (FUSED) {
-                                    const float v = pre_v(a.X[(t0 + t) * (int64_t)a.K + k], a.relu2);
+                                    const float* xr = a.X + (t0 + t) * x_stride(a);
+                                    const float v = act_v(xr[k], a.act == 2 ? xr[a.K + k] : 1.0f, a.act);
                                     xv = act_code(norm ? v * a.gain[k] : v, sp[t]);
                                 } else {
                                     xv = a.Xq[(t0 + t) * (int64_t)a.K + k];

@@ -91,6 +91,10 @@ def test_forward_f32_rejects_before_launch(L):
     assert f(P(a + 4), 1, 64, None, 1e-5, 0, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_ALIGN
     assert f(P(a), 1, 64, P(2 * a + 8), 1e-5, 0, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_ALIGN
     assert f(P(a), 1, 64, None, 1e-5, 0, P(3 * a), P(4 * a), 8, P(a), None) == ERR_ALIAS
+    # activation mode outside {0, 1, 2}; gated rows are 2K floats long (Y inside the up half)
+    assert f(P(a), 1, 64, None, 1e-5, 3, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_SHAPE
+    assert f(P(a), 1, 64, None, 1e-5, -1, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_SHAPE
+    assert f(P(a), 1, 64, None, 1e-5, 2, P(3 * a), P(4 * a), 8, P(a + 300), None) == ERR_ALIAS
 
 
 def test_quantize_act_rejects_before_launch(L):
@@ -101,6 +105,9 @@ def test_quantize_act_rejects_before_launch(L):
     assert f(P(a), 0, 64, None, 1e-5, 0, P(2 * a), P(3 * a), None) == ERR_SHAPE
     assert f(P(a + 8), 1, 64, None, 1e-5, 0, P(2 * a), P(3 * a), None) == ERR_ALIGN
     assert f(P(a), 1, 64, None, 1e-5, 0, P(a + 16), P(3 * a), None) == ERR_ALIAS
+    assert f(P(a), 1, 64, None, 1e-5, 3, P(2 * a), P(3 * a), None) == ERR_SHAPE
+    assert f(P(a), 1, 64, None, 1e-5, 2, P(a + 300), P(3 * a), None) == ERR_ALIAS
+    assert f(P(a), 1, 64, None, 1e-5, 2, P(2 * a), P(a + 400), None) == ERR_ALIAS
 
 
 def test_pack_rejects_before_launch(L):

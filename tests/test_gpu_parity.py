@@ -97,6 +97,8 @@ def test_pack_reuses_workspace_and_is_deterministic():
 QUANT_CASES = [
     (1, 4, None), (3, 260, None), (5, 2560, "norm"), (7, 6912, "relu2norm"), (4, 64, "relu2"),
     (64, 2560, None), (512, 6912, None), (16, 28672, "relu2norm"), (33, 8192, "norm"),
+    # gated squared ReLU: rows of [gate | up], 2K values per token
+    (3, 2560, "gated"), (5, 6912, "gatednorm"), (2, 28672, "gatednorm"), (6, 260, "gatednorm"),
 ]
 
 
@@ -105,14 +107,19 @@ def make_acts(M, K, seed, heavy=False):
 
 
 def pro_args(mode, K, seed):
-    gain = datagen.gains(K, seed) if mode in ("norm", "relu2norm") else None
-    relu2 = mode in ("relu2", "relu2norm")
-    return gain, relu2
+    """(gain or None, activation mode 0/1/2) for a test mode name."""
+    gain = datagen.gains(K, seed) if mode in ("norm", "relu2norm", "gatednorm") else None
+    act = 2 if mode in ("gated", "gatednorm") else int(mode in ("relu2", "relu2norm"))
+    return gain, act
+
+
+def row_len(mode, K):
+    return 2 * K if mode in ("gated", "gatednorm") else K
 
 
 @pytest.mark.parametrize("M,K,mode", QUANT_CASES)
 def test_quantize_act_parity(M, K, mode):
-    x = make_acts(M, K, 2000 + M + K, heavy=(M >= 64))
+    x = make_acts(M, row_len(mode, K), 2000 + M + K, heavy=(M >= 64))
     if M > 2:
         x[0, :] = 0.0                           # an all-zero token takes the 1e-8 floor
     gain, relu2 = pro_args(mode, K, 3000 + K)
@@ -135,6 +142,9 @@ def test_quantize_act_golden(golden):
     g = golden["relu2_norm"]
     xq, s = bl.bitlinear_quantize_act(up(np.array(g["U"], np.float32)), up(np.array(g["gain"], np.float32)),
                                       g["eps"], True)
+    assert down(xq).tolist() == g["codes"]
+    g = golden["gated_relu2"]
+    xq, s = bl.bitlinear_quantize_act(up(np.array(g["U"], np.float32)), None, EPS, 2)
     assert down(xq).tolist() == g["codes"]
 
 
@@ -175,13 +185,15 @@ FWD_CASES = [
     (5, 33, 128, "relu2"), (8, 129, 2560, "relu2norm"), (16, 100, 1024, None), (64, 70, 8192, "norm"),
     (1, 300, 28672, "relu2norm"), (2, 17, 16384, None), (3, 5, 65536, None), (6, 40, 192, None),
     (1, 2560, 2560, None),
+    (1, 2560, 6912, "gatednorm"), (4, 70, 2560, "gatednorm"), (2, 33, 260, "gatednorm"),
+    (1, 50, 28672, "gatednorm"), (3, 17, 128, "gated"), (8, 300, 6912, "gatednorm"),
 ]
 
 
 @pytest.mark.parametrize("M,N,K,mode", FWD_CASES)
 def test_forward_parity(M, N, K, mode):
     w = latents(N, K, 4000 + N * 7 + K)
-    x = make_acts(M, K, 5000 + M + K)
+    x = make_acts(M, row_len(mode, K), 5000 + M + K)
     gain, relu2 = pro_args(mode, K, 6000 + K)
     r = run_gpu(x, w, mode, gain, relu2)
     o = oracle.bitlinear(x, w, gain=gain, eps=EPS, relu2=relu2) if mode else oracle.bitlinear(x, w)
