@@ -133,6 +133,22 @@ int bitlinear_forward_f32(const float* X, int64_t M, int64_t K, const float* gai
                           const uint8_t* W_packed, const float* gamma, int64_t N, float* Y,
                           hipStream_t stream);
 
+/*
+ * Residual forms: the product is added to what Y holds,
+ *   Y[t][n] = fl32(Y[t][n] + y[t][n]),   y[t][n] as computed by the call without the suffix,
+ * so a sublayer's output goes into the residual stream of the Transformer block
+ * ("BitNet b1.58 深度解析" s.2.4: a standard Transformer block with every nn.Linear
+ * replaced by BitLinear) without a separate add pass. Y is read and written by the
+ * same thread; it may not overlap any input. Other arguments, layouts and errors as in
+ * bitlinear_forward (without acc) and bitlinear_forward_f32.
+ */
+int bitlinear_forward_residual(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K,
+                               const uint8_t* W_packed, const float* gamma, int64_t N, float* Y,
+                               hipStream_t stream);
+int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const float* gain, float eps,
+                                   int act, const uint8_t* W_packed, const float* gamma, int64_t N,
+                                   float* Y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

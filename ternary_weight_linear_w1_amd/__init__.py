@@ -27,6 +27,8 @@ EXPORTED = (
     "bitlinear_quantize_act",
     "bitlinear_forward",
     "bitlinear_forward_f32",
+    "bitlinear_forward_residual",
+    "bitlinear_forward_f32_residual",
 )
 
 _lib = None
@@ -58,6 +60,10 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward.restype = ci
         L.bitlinear_forward_f32.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, i64, vp, vp]
         L.bitlinear_forward_f32.restype = ci
+        L.bitlinear_forward_residual.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp]
+        L.bitlinear_forward_residual.restype = ci
+        L.bitlinear_forward_f32_residual.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, i64, vp, vp]
+        L.bitlinear_forward_f32_residual.restype = ci
         _lib = L
     return _lib
 
@@ -82,7 +88,9 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _need(t, dtype, name, ndim=None):
+def _need(t, dtype, name, ndim=None, shape=None):
+    """Device, dtype, contiguity and (when given) rank and exact shape of a tensor argument:
+    the library trusts the sizes it is given, so a short buffer must not get through."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -94,6 +102,8 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError("%s must be contiguous" % name)
     if ndim is not None and t.dim() != ndim:
         raise ValueError("%s must have %d dimensions" % (name, ndim))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
 def bitlinear_pack_workspace_bytes(N: int, K: int) -> int:
@@ -107,8 +117,10 @@ def bitlinear_pack_weights(W, packed=None, gamma=None, workspace=None, stream=No
     N, K = W.shape
     if packed is None:
         packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    _need(packed, torch.uint8, "packed", shape=(N, K // 4))
     if gamma is None:
         gamma = torch.empty((1,), dtype=torch.float32, device=W.device)
+    _need(gamma, torch.float32, "gamma", shape=(1,))
     nbytes = bitlinear_pack_workspace_bytes(N, K)
     if workspace is None:
         workspace = torch.empty((max(nbytes, 8),), dtype=torch.uint8, device=W.device)
@@ -137,51 +149,74 @@ def bitlinear_quantize_act(X, gain=None, eps: float = 1e-5, act=0, xq=None, scal
     _need(X, torch.float32, "X", 2)
     act, M, K = _act_mode(act, X)
     if gain is not None:
-        _need(gain, torch.float32, "gain", 1)
+        _need(gain, torch.float32, "gain", shape=(K,))
     if xq is None:
         xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    _need(xq, torch.int8, "xq", shape=(M, K))
     if scale is None:
         scale = torch.empty((M,), dtype=torch.float32, device=X.device)
+    _need(scale, torch.float32, "scale", shape=(M,))
     _check(lib().bitlinear_quantize_act(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(xq),
                                         _ptr(scale), _stream(stream)), "bitlinear_quantize_act")
     return xq, scale
 
 
-def bitlinear_forward(Xq, x_scale, W_packed, gamma, y=None, acc=None, stream=None):
-    """int8 activations + packed ternary weights -> fp32 y [M][N] (and int32 acc if given)."""
+def bitlinear_forward(Xq, x_scale, W_packed, gamma, y=None, acc=None, stream=None, residual=False):
+    """int8 activations + packed ternary weights -> fp32 y [M][N] (and int32 acc if given).
+    residual=True adds the product to the given y (no acc)."""
     import torch
     _need(Xq, torch.int8, "Xq", 2)
-    _need(x_scale, torch.float32, "x_scale", 1)
     _need(W_packed, torch.uint8, "W_packed", 2)
-    _need(gamma, torch.float32, "gamma", 1)
     M, K = Xq.shape
     N = W_packed.shape[0]
     if W_packed.shape[1] * 4 != K:
         raise ValueError("W_packed must have K/4 columns")
+    _need(x_scale, torch.float32, "x_scale", shape=(M,))
+    _need(gamma, torch.float32, "gamma", shape=(1,))
+    if residual:
+        if y is None or acc is not None:
+            raise ValueError("residual needs y and takes no acc")
+        _need(y, torch.float32, "y", shape=(M, N))
+        _check(lib().bitlinear_forward_residual(_ptr(Xq), _ptr(x_scale), M, K, _ptr(W_packed), _ptr(gamma), N,
+                                                _ptr(y), _stream(stream)), "bitlinear_forward_residual")
+        return y
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    _need(y, torch.float32, "y", shape=(M, N))
     if acc is True:
         acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    if isinstance(acc, torch.Tensor):
+        _need(acc, torch.int32, "acc", shape=(M, N))
     _check(lib().bitlinear_forward(_ptr(Xq), _ptr(x_scale), M, K, _ptr(W_packed), _ptr(gamma), N, _ptr(y),
                                    _ptr(acc if acc is not None and acc is not False else None), _stream(stream)),
            "bitlinear_forward")
     return (y, acc) if isinstance(acc, torch.Tensor) else y
 
 
-def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=0, y=None, stream=None):
-    """Fused quantize + product from fp32 activations [M][K] ([M][2K] when act == 2) -> fp32 y [M][N]."""
+def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=0, y=None, stream=None,
+                          residual=False):
+    """Fused quantize + product from fp32 activations [M][K] ([M][2K] when act == 2) -> fp32 y [M][N].
+    residual=True adds the product to the given y."""
     import torch
     _need(X, torch.float32, "X", 2)
     _need(W_packed, torch.uint8, "W_packed", 2)
-    _need(gamma, torch.float32, "gamma", 1)
-    if gain is not None:
-        _need(gain, torch.float32, "gain", 1)
+    _need(gamma, torch.float32, "gamma", shape=(1,))
     act, M, K = _act_mode(act, X)
+    if gain is not None:
+        _need(gain, torch.float32, "gain", shape=(K,))
     N = W_packed.shape[0]
     if W_packed.shape[1] * 4 != K:
         raise ValueError("W_packed must have K/4 columns")
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=X.device)
-    _check(lib().bitlinear_forward_f32(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(W_packed),
-                                       _ptr(gamma), N, _ptr(y), _stream(stream)), "bitlinear_forward_f32")
+    if residual:
+        if y is None:
+            raise ValueError("residual needs y")
+        _need(y, torch.float32, "y", shape=(M, N))
+        fn, name = lib().bitlinear_forward_f32_residual, "bitlinear_forward_f32_residual"
+    else:
+        if y is None:
+            y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+        _need(y, torch.float32, "y", shape=(M, N))
+        fn, name = lib().bitlinear_forward_f32, "bitlinear_forward_f32"
+    _check(fn(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(W_packed), _ptr(gamma), N, _ptr(y), _stream(stream)),
+           name)
     return y

@@ -101,7 +101,16 @@ void launch_k64(const bl::FwdArgs& a, int wg_per_cu, hipStream_t stream)
     const int gx = (int)(passes < max_x ? passes : max_x);
     const int gy = (int)(tiles < 65535 ? tiles : 65535);
     const size_t lds = (size_t)MT * (size_t)a.K;
-    hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, R, FUSED>), dim3(gx, gy), dim3(256), lds, stream, a);
+    if (a.residual) {
+        // (the row loop strides by the grid, so any grid width is correct)
+        if constexpr (MT * R <= 4)
+            hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, R, FUSED, true>), dim3(gx, gy), dim3(256), lds, stream,
+                               a);
+        else
+            hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, 1, FUSED, true>), dim3(gx, gy), dim3(256), lds, stream,
+                               a);
+    } else
+        hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, R, FUSED, false>), dim3(gx, gy), dim3(256), lds, stream, a);
 }
 
 // One token per tile: up to 4 chunks (256 codes) per lane.
@@ -144,7 +153,8 @@ bool dispatch_mt4(const bl::FwdArgs& a, hipStream_t stream)
     const bool big = a.N * (int64_t)a.K >= (int64_t(64) << 20);
     if (KC <= 64) { launch_k64<64, 4, 1, 1, FUSED>(a, 2, stream); return true; }
     if (KC <= 128) {
-        if (big) launch_k64<128, 4, 1, 4, FUSED>(a, 2, stream);
+        // four rows per lane need the registers the residual loads take
+        if (big && !a.residual) launch_k64<128, 4, 1, 4, FUSED>(a, 2, stream);
         else launch_k64<128, 4, 1, 1, FUSED>(a, 2, stream);
         return true;
     }
@@ -167,7 +177,7 @@ void launch_generic(const bl::FwdArgs& a, hipStream_t stream)
 template <int BM, int BN, int WM, int WN, int P, int BK>
 void launch_gemm(const bl::FwdArgs& f, hipStream_t stream)
 {
-    bl::GemmArgs a{f.Xq, f.xscale, f.W, f.gamma, f.Y, f.acc, (int)f.M, (int)f.N, f.K};
+    bl::GemmArgs a{f.Xq, f.xscale, f.W, f.gamma, f.Y, f.acc, (int)f.M, (int)f.N, f.K, f.residual};
     const int64_t tiles = ((f.M + BM - 1) / BM) * ((f.N + BN - 1) / BN);
     hipLaunchKernelGGL((bl::gemm_mfma_kernel<BM, BN, WM, WN, P, false, BK>), dim3((unsigned)tiles), dim3(256), 0,
                        stream, a);
@@ -206,6 +216,84 @@ void dispatch_forward(const bl::FwdArgs& a, bool chunk_ok, hipStream_t stream)
             return;
     }
     launch_generic<FUSED>(a, stream);
+}
+
+int forward_impl(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed,
+                 const float* gamma, int64_t N, float* Y, int32_t* acc, int residual, hipStream_t stream)
+{
+    if (!Xq || !x_scale || !W_packed || !gamma || !Y)
+        return BITLINEAR_ERR_NULL;
+    int st = check_mk(M, K);
+    if (st != BITLINEAR_OK)
+        return st;
+    if ((st = check_nk(N, K)) != BITLINEAR_OK)
+        return st;
+    if (M > kMaxElems / N)
+        return BITLINEAR_ERR_SHAPE;
+    if (!aligned(Xq, 4) || !aligned(x_scale, 4) || !aligned(W_packed, 1) || !aligned(gamma, 4) ||
+        !aligned(Y, 4) || (acc && !aligned(acc, 4)))
+        return BITLINEAR_ERR_ALIGN;
+    const int64_t ybytes = M * N * 4;
+    const void* ins[4] = {Xq, x_scale, W_packed, gamma};
+    const int64_t insz[4] = {M * K, M * 4, N * (K / 4), 4};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(Y, ybytes, ins[i], insz[i]) || overlap(acc, ybytes, ins[i], insz[i]))
+            return BITLINEAR_ERR_ALIAS;
+    if (overlap(Y, ybytes, acc, ybytes))
+        return BITLINEAR_ERR_ALIAS;
+    bl::FwdArgs a{};
+    a.Xq = Xq;
+    a.xscale = x_scale;
+    a.W = W_packed;
+    a.gamma = gamma;
+    a.Y = Y;
+    a.acc = acc;
+    a.M = M;
+    a.N = N;
+    a.K = (int)K;
+    a.residual = residual;
+    const bool chunk_ok = (K % 64) == 0 && aligned(W_packed, 16) && aligned(Xq, 16);
+    if (!(chunk_ok && dispatch_gemm(a, stream)))
+        dispatch_forward<false>(a, chunk_ok, stream);
+    return launched();
+}
+
+int forward_f32_impl(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
+                     const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int residual,
+                     hipStream_t stream)
+{
+    if (!X || !W_packed || !gamma || !Y)
+        return BITLINEAR_ERR_NULL;
+    int st = check_mk(M, K);
+    if (st != BITLINEAR_OK)
+        return st;
+    if ((st = check_nk(N, K)) != BITLINEAR_OK)
+        return st;
+    if (M > kMaxElems / N || act < 0 || act > 2 || (act == 2 && M > kMaxElems / (2 * K)))
+        return BITLINEAR_ERR_SHAPE;
+    if (!aligned(X, 16) || (gain && !aligned(gain, 16)) || !aligned(gamma, 4) || !aligned(Y, 4))
+        return BITLINEAR_ERR_ALIGN;
+    const int64_t ybytes = M * N * 4;
+    const void* ins[4] = {X, gain, W_packed, gamma};
+    const int64_t insz[4] = {M * K * 4 * (act == 2 ? 2 : 1), K * 4, N * (K / 4), 4};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(Y, ybytes, ins[i], insz[i]))
+            return BITLINEAR_ERR_ALIAS;
+    bl::FwdArgs a{};
+    a.X = X;
+    a.gain = gain;
+    a.eps = eps;
+    a.act = act;
+    a.W = W_packed;
+    a.gamma = gamma;
+    a.Y = Y;
+    a.M = M;
+    a.N = N;
+    a.K = (int)K;
+    a.residual = residual;
+    const bool chunk_ok = (K % 64) == 0 && aligned(W_packed, 16);
+    dispatch_forward<true>(a, chunk_ok, stream);
+    return launched();
 }
 
 }  // namespace
@@ -303,76 +391,26 @@ int bitlinear_quantize_act(const float* X, int64_t M, int64_t K, const float* ga
 int bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed,
                       const float* gamma, int64_t N, float* Y, int32_t* acc, hipStream_t stream)
 {
-    if (!Xq || !x_scale || !W_packed || !gamma || !Y)
-        return BITLINEAR_ERR_NULL;
-    int st = check_mk(M, K);
-    if (st != BITLINEAR_OK)
-        return st;
-    if ((st = check_nk(N, K)) != BITLINEAR_OK)
-        return st;
-    if (M > kMaxElems / N)
-        return BITLINEAR_ERR_SHAPE;
-    if (!aligned(Xq, 4) || !aligned(x_scale, 4) || !aligned(W_packed, 1) || !aligned(gamma, 4) ||
-        !aligned(Y, 4) || (acc && !aligned(acc, 4)))
-        return BITLINEAR_ERR_ALIGN;
-    const int64_t ybytes = M * N * 4;
-    const void* ins[4] = {Xq, x_scale, W_packed, gamma};
-    const int64_t insz[4] = {M * K, M * 4, N * (K / 4), 4};
-    for (int i = 0; i < 4; ++i)
-        if (overlap(Y, ybytes, ins[i], insz[i]) || overlap(acc, ybytes, ins[i], insz[i]))
-            return BITLINEAR_ERR_ALIAS;
-    if (overlap(Y, ybytes, acc, ybytes))
-        return BITLINEAR_ERR_ALIAS;
-    bl::FwdArgs a{};
-    a.Xq = Xq;
-    a.xscale = x_scale;
-    a.W = W_packed;
-    a.gamma = gamma;
-    a.Y = Y;
-    a.acc = acc;
-    a.M = M;
-    a.N = N;
-    a.K = (int)K;
-    const bool chunk_ok = (K % 64) == 0 && aligned(W_packed, 16) && aligned(Xq, 16);
-    if (!(chunk_ok && dispatch_gemm(a, stream)))
-        dispatch_forward<false>(a, chunk_ok, stream);
-    return launched();
+    return forward_impl(Xq, x_scale, M, K, W_packed, gamma, N, Y, acc, 0, stream);
+}
+
+int bitlinear_forward_residual(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K,
+                               const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, hipStream_t stream)
+{
+    return forward_impl(Xq, x_scale, M, K, W_packed, gamma, N, Y, nullptr, 1, stream);
 }
 
 int bitlinear_forward_f32(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
                           const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, hipStream_t stream)
 {
-    if (!X || !W_packed || !gamma || !Y)
-        return BITLINEAR_ERR_NULL;
-    int st = check_mk(M, K);
-    if (st != BITLINEAR_OK)
-        return st;
-    if ((st = check_nk(N, K)) != BITLINEAR_OK)
-        return st;
-    if (M > kMaxElems / N || act < 0 || act > 2 || (act == 2 && M > kMaxElems / (2 * K)))
-        return BITLINEAR_ERR_SHAPE;
-    if (!aligned(X, 16) || (gain && !aligned(gain, 16)) || !aligned(gamma, 4) || !aligned(Y, 4))
-        return BITLINEAR_ERR_ALIGN;
-    const int64_t ybytes = M * N * 4;
-    const void* ins[4] = {X, gain, W_packed, gamma};
-    const int64_t insz[4] = {M * K * 4 * (act == 2 ? 2 : 1), K * 4, N * (K / 4), 4};
-    for (int i = 0; i < 4; ++i)
-        if (overlap(Y, ybytes, ins[i], insz[i]))
-            return BITLINEAR_ERR_ALIAS;
-    bl::FwdArgs a{};
-    a.X = X;
-    a.gain = gain;
-    a.eps = eps;
-    a.act = act;
-    a.W = W_packed;
-    a.gamma = gamma;
-    a.Y = Y;
-    a.M = M;
-    a.N = N;
-    a.K = (int)K;
-    const bool chunk_ok = (K % 64) == 0 && aligned(W_packed, 16);
-    dispatch_forward<true>(a, chunk_ok, stream);
-    return launched();
+    return forward_f32_impl(X, M, K, gain, eps, act, W_packed, gamma, N, Y, 0, stream);
+}
+
+int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
+                                   const uint8_t* W_packed, const float* gamma, int64_t N, float* Y,
+                                   hipStream_t stream)
+{
+    return forward_f32_impl(X, M, K, gain, eps, act, W_packed, gamma, N, Y, 1, stream);
 }
 
 }  // extern "C"

@@ -32,11 +32,12 @@ struct GemmArgs {
     const float* xscale;  // [M]
     const uint8_t* W;     // [N][K/4]
     const float* gamma;   // [1]
-    float* Y;             // [M][N]
+    float* Y;             // [M][N]; with `residual` read and overwritten by Y + product
     int32_t* acc;         // [M][N] or null
     int M;
     int N;
     int K;
+    int residual;         // 1: Y[m][n] = fl32(Y[m][n] + y[m][n])
 };
 
 // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous range of tiles
@@ -263,7 +264,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
                     if (n < N) {
                         const int32_t v = C[fm][fn][r] - off;
                         const int64_t o = (int64_t)m * N + n;
-                        a.Y[o] = (float)v * c;
+                        const float yv = (float)v * c;
+                        a.Y[o] = a.residual ? a.Y[o] + yv : yv;
                         if (a.acc)
                             a.acc[o] = v;
                     }

@@ -34,11 +34,12 @@ struct FwdArgs {
     int act;               // activation (fused): 0 identity, 1 squared ReLU, 2 gated
     const uint8_t* W;      // packed [N][K/4]
     const float* gamma;    // [1]
-    float* Y;              // [M][N]
+    float* Y;              // [M][N]; with `residual` read and overwritten by Y + product
     int32_t* acc;          // [M][N] or null
     int64_t M;
     int64_t N;
     int K;
+    int residual;          // 1: Y[t][n] = fl32(Y[t][n] + y[t][n])
 };
 
 // Codes of float4 group g (elements 4g..4g+3) as one little-endian dword (natural order).
@@ -183,8 +184,10 @@ constexpr int kOob = 0x7ffffff0;       // an offset past every buffer: loads giv
 // computed. Weights are read and outputs written with raw buffer instructions whose
 // descriptor is rebased per pass; lanes without a valid chunk or row use an offset past
 // the end (hardware zero-fill / dropped store), so the loop has no branches and the
-// outstanding-load counts stay exact.
-template <int L, int MT, int CPL, int R, bool FUSED>
+// outstanding-load counts stay exact. With RES the old outputs of a pass are loaded
+// just before its weights (in-order completion: waiting for the weights covers them)
+// and the product is added to them.
+template <int L, int MT, int CPL, int R, bool FUSED, bool RES>
 __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
 {
     constexpr int NT = 256;
@@ -211,7 +214,19 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
             const int c = j + i * L;
             woff[r][i] = c < KC ? (slot + r * RG) * KB + c * 16 : kOob;
         }
-    auto load_pass = [&](int64_t rb, u32x4 (&w)[R][CPL]) {
+    auto load_pass = [&](int64_t rb, u32x4 (&w)[R][CPL], float (&yo)[R][MT], __amdgpu_buffer_rsrc_t ry, int mt) {
+        if constexpr (RES) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int64_t row = rb + slot + (int64_t)r * RG;
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    const bool mine = j == 0 && row < N && t < mt;
+                    yo[r][t] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(ry, mine ? (int)((t * N + row) * 4) : kOob, 0, 0));
+                }
+            }
+        }
         const int64_t rows = rb < N ? ((N - rb) < RPP ? (N - rb) : RPP) : 0;
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (rb < N ? rb : 0) * KB), (short)0, (int)(rows * KB), kBufFlags);
@@ -228,13 +243,21 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
         const int64_t pstride = (int64_t)gridDim.x * RPP;
         int64_t rb = (int64_t)blockIdx.x * RPP;
 
+        // Outputs of this token tile: y (and acc when requested; otherwise a zero-size
+        // buffer that drops every store).
+        const __amdgpu_buffer_rsrc_t ry =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.Y + t0 * N), (short)0, (int)(mt * N * 4), kBufFlags);
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            a.acc ? (void*)(a.acc + t0 * N) : (void*)a.Y, (short)0, a.acc ? (int)(mt * N * 4) : 0, kBufFlags);
+
         // Activations of token 0 first, then the first two passes of weights, then the
         // prologue arithmetic while the weights are in flight.
         Pre pre;
         stage_preload<FUSED>(a, t0, pre);
         u32x4 cur[R][CPL], nxt[R][CPL];
-        load_pass(rb, cur);
-        load_pass(rb + pstride, nxt);
+        float ycur[R][MT], ynxt[R][MT];
+        load_pass(rb, cur, ycur, ry, mt);
+        load_pass(rb + pstride, nxt, ynxt, ry, mt);
 
         float s[MT];
         __syncthreads();  // LDS of the previous tile is no longer read
@@ -271,14 +294,7 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
             csc[t] = gamma / s[t];
         }
 
-        // Outputs of this token tile: y (and acc when requested; otherwise a zero-size
-        // buffer that drops every store).
-        const __amdgpu_buffer_rsrc_t ry =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(a.Y + t0 * N), (short)0, (int)(mt * N * 4), kBufFlags);
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            a.acc ? (void*)(a.acc + t0 * N) : (void*)a.Y, (short)0, a.acc ? (int)(mt * N * 4) : 0, kBufFlags);
-
-        auto compute_pass = [&](int64_t pb, const u32x4 (&w)[R][CPL]) {
+        auto compute_pass = [&](int64_t pb, const u32x4 (&w)[R][CPL], const float (&yo)[R][MT]) {
             int32_t accv[R][MT];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -331,7 +347,10 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
                 for (int t = 0; t < MT; ++t) {
                     const bool mine = j == 0 && row < N && t < mt;
                     const int off = mine ? (int)((t * N + row) * 4) : kOob;
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, (float)accv[r][t] * csc[t]), ry, off, 0, 0);
+                    float yv = (float)accv[r][t] * csc[t];
+                    if constexpr (RES)
+                        yv = yo[r][t] + yv;
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, yv), ry, off, 0, 0);
                     __builtin_amdgcn_raw_buffer_store_b32(accv[r][t], ra, off, 0, 0);
                 }
             }
@@ -340,12 +359,12 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
         // Two named buffers in turn (no register copy at the loop edge), so each wait
         // for weight data sits right before its use; two passes are in flight.
         for (; rb < N; rb += 2 * pstride) {
-            compute_pass(rb, cur);
-            load_pass(rb + 2 * pstride, cur);
+            compute_pass(rb, cur, ycur);
+            load_pass(rb + 2 * pstride, cur, ycur, ry, mt);
             if (rb + pstride >= N)
                 break;
-            compute_pass(rb + pstride, nxt);
-            load_pass(rb + 3 * pstride, nxt);
+            compute_pass(rb + pstride, nxt, ynxt);
+            load_pass(rb + 3 * pstride, nxt, ynxt, ry, mt);
         }
     }
 }
@@ -416,7 +435,8 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(FwdArgs a)
             if (lane == 0 && row < a.N) {
                 for (int t = 0; t < mt; ++t) {
                     const int64_t o = (t0 + t) * a.N + row;
-                    a.Y[o] = (float)accv[t] * csc[t];
+                    const float yv = (float)accv[t] * csc[t];
+                    a.Y[o] = a.residual ? a.Y[o] + yv : yv;
                     if (a.acc)
                         a.acc[o] = accv[t];
                 }

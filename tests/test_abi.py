@@ -97,6 +97,19 @@ def test_forward_f32_rejects_before_launch(L):
     assert f(P(a), 1, 64, None, 1e-5, 2, P(3 * a), P(4 * a), 8, P(a + 300), None) == ERR_ALIAS
 
 
+def test_residual_forms_reject_before_launch(L):
+    a = 1 << 20
+    f = L.bitlinear_forward_residual
+    assert f(None, P(2 * a), 1, 64, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_NULL
+    assert f(P(a), P(2 * a), 1, 62, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_SHAPE
+    assert f(P(a), P(2 * a), 1, 64, P(3 * a), P(4 * a), 8, P(5 * a + 2), None) == ERR_ALIGN
+    assert f(P(a), P(2 * a), 1, 64, P(3 * a), P(4 * a), 8, P(3 * a), None) == ERR_ALIAS
+    g = L.bitlinear_forward_f32_residual
+    assert g(P(a), 1, 64, None, 1e-5, 0, None, P(4 * a), 8, P(5 * a), None) == ERR_NULL
+    assert g(P(a), 1, 64, None, 1e-5, 5, P(3 * a), P(4 * a), 8, P(5 * a), None) == ERR_SHAPE
+    assert g(P(a), 1, 64, None, 1e-5, 0, P(3 * a), P(4 * a), 8, P(a), None) == ERR_ALIAS
+
+
 def test_quantize_act_rejects_before_launch(L):
     f = L.bitlinear_quantize_act
     a = 1 << 20

@@ -249,3 +249,71 @@ def test_gemm_parity(M, N, K):
     assert np.array_equal(down(xq), o["xq"])
     assert np.array_equal(down(acc), o["acc"])
     assert np.array_equal(down(y).view(np.int32), o["y"].view(np.int32))
+
+
+# ------------------------------------------------------------------------------ residual forms
+
+RESIDUAL_CASES = [
+    # (M, N, K, mode): GEMV tiles of 1, 2 and 4 tokens incl. the large-K tiles, the
+    # generic path (K % 64 != 0), the MFMA path (M >= 16), fused prologue modes
+    (1, 2560, 2560, "norm"), (1, 2560, 6912, "relu2norm"), (1, 300, 6912, "gatednorm"), (2, 70, 2560, None),
+    (4, 129, 8192, None), (3, 6912, 6912, None), (1, 37, 260, "norm"), (5, 33, 260, None), (64, 200, 2560, None),
+    (16, 33, 64, None), (1, 1024, 28672, None),
+]
+
+
+def oracle_residual(y0, y_ora):
+    return (y0.astype(np.float32) + y_ora.astype(np.float32)).astype(np.float32)
+
+
+@pytest.mark.parametrize("M,N,K,mode", RESIDUAL_CASES)
+def test_residual_parity(M, N, K, mode):
+    """Y + product: bit for bit equal to adding the plain call's output in fp32, and
+    against the oracle bit-exact on the plain path, within the 1e-6 output tolerance
+    (plus the add's own rounding) on the RMSNorm path."""
+    w = latents(N, K, 9100 + N + K)
+    x = make_acts(M, row_len(mode, K), 9200 + M + K)
+    gain, act = pro_args(mode, K, 9300 + K)
+    y0 = datagen.outlier_acts(M, N, 9400 + M + N)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    xg, gg = up(x), None if gain is None else up(gain)
+    if mode is None:
+        o = oracle.bitlinear(x, w)
+        xq, s = bl.bitlinear_quantize_act(xg)
+    else:
+        o = oracle.bitlinear(x, w, gain=gain, eps=EPS, relu2=act)
+        xq, s = bl.bitlinear_quantize_act(xg, gg, EPS, act)
+    expect = oracle_residual(y0, o["y"])
+    ya = up(y0)
+    bl.bitlinear_forward(xq, s, packed, gamma, y=ya, residual=True)
+    yb = up(y0)
+    bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, act, y=yb, residual=True)
+    plain = bl.bitlinear_forward(xq, s, packed, gamma)
+    ra, rb, rp = down(ya), down(yb), down(plain)
+    same = oracle_residual(y0, rp)
+    assert np.array_equal(ra.view(np.int32), same.view(np.int32))
+    assert np.array_equal(rb.view(np.int32), same.view(np.int32))
+    if gain is None:
+        assert np.array_equal(ra.view(np.int32), expect.view(np.int32))
+    else:
+        tol = 1e-6 * np.abs(o["y"].astype(np.float64)) + 2.0 ** -23 * np.abs(expect.astype(np.float64))
+        assert (np.abs(ra.astype(np.float64) - expect.astype(np.float64)) <= tol).all()
+
+
+def test_binding_rejects_short_buffers():
+    """The library trusts the sizes it is given; the binding checks every buffer's shape."""
+    w = latents(40, 256, 21)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    x = up(make_acts(3, 256, 22))
+    xq, s = bl.bitlinear_quantize_act(x)
+    with pytest.raises(ValueError):
+        bl.bitlinear_forward(xq, s, packed, gamma, y=torch.empty((3, 39), dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        bl.bitlinear_forward(xq, s[:2], packed, gamma)
+    with pytest.raises(ValueError):
+        bl.bitlinear_forward_f32(x, packed, gamma, torch.ones(255, device=DEV))
+    with pytest.raises(ValueError):
+        bl.bitlinear_quantize_act(x, xq=torch.empty((3, 255), dtype=torch.int8, device=DEV))
+    with pytest.raises(ValueError):
+        bl.bitlinear_forward(xq, s, packed, gamma, y=torch.empty((3, 40), dtype=torch.float32, device=DEV),
+                             residual=True, acc=True)
