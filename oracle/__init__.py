@@ -172,3 +172,45 @@ def bitlinear(x: np.ndarray, w: np.ndarray, gain=None, eps: float = 1e-5, relu2=
         xq, s = quantize_act_norm(x, gain, eps, relu2)
     acc, y = forward(xq, s, q, gamma)
     return dict(packed=packed, gamma=gamma, q=q, xq=xq, s=s, acc=acc, y=y)
+
+
+def attention_ctx1(qkv: np.ndarray, heads: int, kv_heads: int, head_dim: int) -> np.ndarray:
+    """Scaled dot-product attention over a single position (BitNet b1.58 深度解析 s.2.4 block
+    diagram; grouped-query heads): the softmax over one key is exactly 1 and rotary
+    embedding at position 0 is the identity, so each query head outputs the value vector
+    of its KV group. Written out literally as softmax-weighted values (no shortcut)."""
+    m = qkv.shape[0]
+    q_end, k_end = heads * head_dim, (heads + kv_heads) * head_dim
+    v = qkv[:, k_end:].reshape(m, kv_heads, head_dim)
+    k = qkv[:, q_end:k_end].reshape(m, kv_heads, head_dim)
+    q = qkv[:, :q_end].reshape(m, heads, head_dim)
+    out = np.empty((m, heads, head_dim), dtype=np.float32)
+    group = heads // kv_heads
+    for t in range(m):
+        for hh in range(heads):
+            g = hh // group
+            score = np.array([np.dot(q[t, hh].astype(np.float64), k[t, g].astype(np.float64))]) / np.sqrt(head_dim)
+            p = np.exp(score - score.max())
+            p /= p.sum()                                  # one key: p == [1.0]
+            out[t, hh] = (p[0] * v[t, g].astype(np.float64)).astype(np.float32)
+    return out.reshape(m, heads * head_dim)
+
+
+def decode_layer(h: np.ndarray, mats: dict, gains: dict, dims: dict, gated: bool, eps: float = 1e-5):
+    """One BitNet decode layer on fp32 h [M][H] (standard Transformer block with BitLinear
+    in place of nn.Linear: BitNet b1.58 深度解析 s.2.4; subln before O and down and ReLU^2:
+    微软AI大模型炸场 s.1-2). mats[name] = (codes int8 [N][K], gamma) for qkv, o, up
+    ([2F][K] gate rows then up rows when gated), down; gains g_in, g_attn, g_post, g_ffn.
+    Residual adds are fp32. Returns the new h and the intermediates."""
+    def lin(x, name, gain, act):
+        q, gamma = mats[name]
+        xq, s = quantize_act_norm(x, gain, eps, act)
+        return forward(xq, s, q, gamma)[1]
+
+    f32 = np.float32
+    qkv = lin(h, "qkv", gains["g_in"], 0)
+    o = attention_ctx1(qkv, dims["heads"], dims["kv_heads"], dims["head_dim"])
+    h1 = (h.astype(f32) + lin(o, "o", gains["g_attn"], 0)).astype(f32)
+    u = lin(h1, "up", gains["g_post"], 0)
+    h2 = (h1 + lin(u, "down", gains["g_ffn"], 2 if gated else 1)).astype(f32)
+    return h2, dict(qkv=qkv, o=o, h1=h1, u=u)

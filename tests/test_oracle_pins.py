@@ -349,3 +349,84 @@ def test_gated_codes_are_plain_codes_of_the_product(ora):
     sp = F32(127.0) / np.maximum(np.abs((v * g).astype(np.float32)).max(axis=1), F32(1e-8))
     ref = sp.astype(np.float64) * np.sqrt(ms + float(F32(1e-5)))
     assert np.allclose(s.astype(np.float64), ref, rtol=2e-7, atol=0)
+
+
+# ----------------------------------------------------------------------------- decode layer
+
+def test_attention_ctx1_hand_example(ora):
+    """heads 4, kv_heads 2, head_dim 1: qkv = [q0..q3 | k0 k1 | v0 v1]; query heads 0, 1
+    share KV head 0 and heads 2, 3 share KV head 1, and one key gets softmax weight 1,
+    so o = [v0, v0, v1, v1] whatever q and k are."""
+    qkv = np.array([[9.0, -3.0, 0.5, 7.0, 2.0, -8.0, 1.25, -6.5]], np.float32)
+    assert ora.attention_ctx1(qkv, 4, 2, 1).tolist() == [[1.25, 1.25, -6.5, -6.5]]
+
+
+def test_attention_ctx1_ignores_q_and_k_and_reduces_to_v_for_mha(ora):
+    rng = np.random.default_rng(61)
+    qkv = rng.standard_normal((3, (6 + 2 * 6) * 16)).astype(np.float32)
+    o = ora.attention_ctx1(qkv, 6, 6, 16)
+    assert np.array_equal(o, qkv[:, 12 * 16:])          # one KV head per query head: o = v
+    qkv2 = qkv.copy()
+    qkv2[:, :12 * 16] = rng.standard_normal((3, 12 * 16)) * 50
+    assert np.array_equal(ora.attention_ctx1(qkv2, 6, 6, 16), o)
+
+
+def _layer(ora, H, F, heads, kv, hd, gated, seed, zero=()):
+    mats = {}
+    shapes = {"qkv": ((heads + 2 * kv) * hd, H), "o": (H, H), "up": ((2 if gated else 1) * F, H), "down": (H, F)}
+    for i, (name, (n, k)) in enumerate(shapes.items()):
+        w = np.zeros((n, k), np.float32) if name in zero else datagen.gg_weights(n, k, seed + i)
+        packed, gamma, q = ora.pack_weights(w)
+        mats[name] = (q, gamma)
+    gains = {g: datagen.gains(H if g != "g_ffn" else F, seed + 10 + j)
+             for j, g in enumerate(("g_in", "g_attn", "g_post", "g_ffn"))}
+    return mats, gains, dict(heads=heads, kv_heads=kv, head_dim=hd)
+
+
+def test_decode_layer_with_zero_weights_is_identity(ora):
+    """All-zero weights give gamma = 1e-8, codes 0 and products 0, so both residual adds
+    leave h unchanged; the intermediates are exact zeros."""
+    mats, gains, dims = _layer(ora, 64, 96, 4, 2, 16, False, 70, zero=("qkv", "o", "up", "down"))
+    h = datagen.outlier_acts(2, 64, 71)
+    h2, mid = ora.decode_layer(h, mats, gains, dims, gated=False)
+    assert np.array_equal(h2, h) and not mid["qkv"].any() and not mid["u"].any()
+
+
+def test_decode_layer_zero_up_rows_skip_the_ffn(ora):
+    """Gated: with the gate|up matrix zero the FFN input relu(gate)^2 * up is 0, down adds
+    exactly 0 and h after the layer equals h after attention; with O also zero it equals
+    the input."""
+    mats, gains, dims = _layer(ora, 64, 96, 4, 1, 16, True, 80, zero=("up",))
+    h = datagen.outlier_acts(3, 64, 81)
+    h2, mid = ora.decode_layer(h, mats, gains, dims, gated=True)
+    assert np.array_equal(h2, mid["h1"])
+    assert not np.array_equal(mid["h1"], h)
+    mats, gains, dims = _layer(ora, 64, 96, 4, 1, 16, True, 80, zero=("up", "o"))
+    h2, _ = ora.decode_layer(h, mats, gains, dims, gated=True)
+    assert np.array_equal(h2, h)
+
+
+def test_decode_layer_matches_dense_fp64_of_dequantized_operands(ora):
+    """Each sublayer of the layer is within the output tolerance of dense fp64 arithmetic on
+    the dequantized operands (codes * gamma) . (xq / s), evaluated on the oracle's own
+    intermediates: checks the residual wiring, the gains and the attention copy."""
+    H, F = 128, 192
+    mats, gains, dims = _layer(ora, H, F, 4, 2, 32, False, 90)
+    h = datagen.outlier_acts(2, H, 91)
+    h2, mid = ora.decode_layer(h, mats, gains, dims, gated=False)
+
+    def dense(x, name, gain, act):
+        q, gamma = mats[name]
+        xq, s = ora.quantize_act_norm(x, gain, 1e-5, act)
+        return (xq.astype(np.float64) / s.astype(np.float64)[:, None]) @ (q.astype(np.float64) * float(gamma)).T
+
+    def close(a, b, scale):
+        return (np.abs(a.astype(np.float64) - b) <= 1e-5 * scale + 1e-6 * np.abs(b)).all()
+
+    qkv = dense(h, "qkv", gains["g_in"], 0)
+    assert close(mid["qkv"], qkv, np.abs(qkv).max())
+    assert np.array_equal(mid["o"][:, :32], mid["qkv"][:, 192:224])    # head 0 <- KV head 0's v
+    d_o = dense(mid["o"], "o", gains["g_attn"], 0)
+    assert close(mid["h1"], h.astype(np.float64) + d_o, np.abs(d_o).max())
+    d_d = dense(mid["u"], "down", gains["g_ffn"], 1)
+    assert close(h2, mid["h1"].astype(np.float64) + d_d, np.abs(d_d).max())
