@@ -68,10 +68,13 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def layer_bytes(N, K, M, mode, fused=True):
-    b = N * K // 4 + 4 + 4 * M * N
-    b += 4 * M * K if fused else (M * K + 4 * M)
-    if mode in ("norm", "relu2norm") and fused:
+def layer_bytes(N, K, M, mode, fused=True, residual=False):
+    """Algorithmic HBM bytes of one BitLinear: packed weights, gamma, activations in
+    (fp32 through the prologue, [gate | up] rows of 2K when gated, or int8 codes and
+    scales), the gain, and the fp32 output (read and written again by a residual add)."""
+    b = N * K // 4 + 4 + 4 * M * N * (2 if residual else 1)
+    b += 4 * M * K * (2 if mode == "gatednorm" else 1) if fused else (M * K + 4 * M)
+    if mode in ("norm", "relu2norm", "gatednorm") and fused:
         b += 4 * K
     return b
 
@@ -439,6 +442,10 @@ def run_extra(torch, bl, datagen, dev, mats2b):
             del m
         res["2B_prefill_M%d" % M] = r
         log("extra prefill M=%d: %s" % (M, r))
+    # ---- decode stack: 30 layers of the 2B shapes at M = 1, plain and gated FFN
+    for gated in (False, True):
+        res["2B_stack30_M1" + ("_gated" if gated else "")] = run_stack(torch, bl, datagen, dev, gated)
+        torch.cuda.empty_cache()
     # ---- packing rate (100B up projection)
     N, K = 28672, 8192
     w = datagen.gg_weights_torch(N, K, datagen.stream_id(5, 9, 0, 0), dev)
@@ -451,6 +458,65 @@ def run_extra(torch, bl, datagen, dev, mats2b):
     del w, packed, ws
     torch.cuda.empty_cache()
     return res
+
+
+STACK_DIMS = dict(hidden=2560, heads=20, kv_heads=5, head_dim=128, ffn=6912)
+
+
+def run_stack(torch, bl, datagen, dev, gated, n_layers=30, copies=2, replays=20):
+    """Per-token latency of a 30-layer decode stack (one launch per BitLinear plus the
+    attention copy), as a HIP graph over `copies` weight copies of the stack so that each
+    pass streams its weights from HBM (>= 776 MB against 256 MB of MALL)."""
+    from ternary_weight_linear_w1_amd.decode_stack import DecodeStack, LayerWeights
+    d = STACK_DIMS
+    H, F = d["hidden"], d["ffn"]
+    nqkv = (d["heads"] + 2 * d["kv_heads"]) * d["head_dim"]
+    shapes = [("qkv", nqkv, H, "norm", False), ("o", H, H, "norm", True),
+              ("up", (2 if gated else 1) * F, H, "norm", False),
+              ("down", H, F, "gatednorm" if gated else "relu2norm", True)]
+    base = []
+    for li in range(n_layers):
+        mats = {}
+        for mi, (name, N, K, mode, _) in enumerate(shapes):
+            w = datagen.gg_weights_torch(N, K, datagen.stream_id(3, li, mi, 0), dev)
+            mats[name] = bl.bitlinear_pack_weights(w)
+            del w
+        gains = {g: datagen.gains_torch(F if g == "g_ffn" else H, datagen.stream_id(3, li, 4 + j, 2), dev)
+                 for j, g in enumerate(("g_in", "g_attn", "g_post", "g_ffn"))}
+        base.append((mats, gains))
+    stacks = []
+    for c in range(copies):
+        layers = [LayerWeights(*[(m[n][0] if c == 0 else m[n][0].clone(), m[n][1]) for n in ("qkv", "o", "up", "down")],
+                               **g) for m, g in base]
+        st = DecodeStack(layers, H, d["heads"], d["kv_heads"], d["head_dim"], F, gated, M=1, eps=EPS, device=dev)
+        st.h.copy_(datagen.outlier_acts_torch(1, H, datagen.stream_id(3, 200, c, 1), dev))
+        stacks.append(st)
+    for st in stacks:
+        st.step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for st in stacks:
+            st.step(stream=torch.cuda.current_stream())
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    per_token = e0.elapsed_time(e1) * 1e-3 / (replays * copies)
+    finite = all(bool(torch.isfinite(st.h).all()) for st in stacks)
+    nbytes = n_layers * sum(layer_bytes(N, K, 1, mode, residual=res) for _, N, K, mode, res in shapes)
+    packed = n_layers * sum(N * K // 4 for _, N, K, _, _ in shapes)
+    out = {"us_per_token": round(per_token * 1e6, 1), "GB/s": round(nbytes / per_token / 1e9, 1),
+           "frac_hbm": round(nbytes / per_token / 1e9 / HBM_PEAK_GBS, 4), "packed_MB": round(packed / 1e6, 1),
+           "algorithmic_MB": round(nbytes / 1e6, 1), "launches_per_token": 5 * n_layers,
+           "ideal_us_at_8TBs": round(nbytes / HBM_PEAK_GBS / 1e3, 1), "h_finite": finite}
+    log("extra stack%s: %s" % (" gated" if gated else "", out))
+    del g, stacks, base
+    return out
 
 
 if __name__ == "__main__":
