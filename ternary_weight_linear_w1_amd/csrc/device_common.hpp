@@ -15,14 +15,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kFloor = 1e-8f;  // floor of max|x| and of gamma
 constexpr int kWave = 64;
 
-__device__ __forceinline__ float wave_max(float v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v = fmaxf(v, __shfl_xor(v, m));
-    return v;
-}
-
 // int8 code of one activation: clip(round_half_even(v * s), -128, 127). One fp32
 // multiply, v_rndne_f32, then a clamp.
 __device__ __forceinline__ int act_code(float v, float s)
@@ -69,17 +61,73 @@ __device__ __forceinline__ void transpose_bytes(uint32_t e0, uint32_t e1, uint32
 }
 
 // ------------------------------------------------------------------------------------
+// Wave reductions through DPP (row-local lane exchange, no LDS traffic). Each step adds
+// a lane's value to its partner's; partners hold the same two operands, so after a step
+// both hold the same bits (addition is commutative). Rows of 16 lanes are combined
+// through readlane in the fixed order (r0 + r1) + (r2 + r3).
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+    v = v + dpp_f64<0xB1>(v);
+    v = v + dpp_f64<0x4E>(v);
+    v = v + dpp_f64<0x141>(v);
+    v = v + dpp_f64<0x140>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// ------------------------------------------------------------------------------------
 // Per-token statistics of the (activation + gain) input, shared by the standalone
-// quantizer and the fused GEMV prologue so that both produce the same bits.
+// quantizer and the fused GEMV prologue so that both produce the same bits. Blocks of
+// 256 threads.
 //
 //   m     = max_k |w_k|,  w_k = act_v(u_k, up_k) * gain_k   (order-free)
-//   sumsq = sum_k v_k^2 in binary64 over 256 virtual lanes: virtual lane l adds the
-//           float4 groups g = l, l+256, l+512, ... in increasing order (components in
-//           order), then the 256 lane sums are combined as a pairwise tree in lane
-//           order. The tree is independent of the real block size NT (64 or 256).
-// With NT == 256 the w values of the first KEEP groups of each thread (g = tid + 256 i,
-// i < KEEP) are returned in `wk` so the caller can quantize them without re-reading.
-// Must be called by all NT threads of the block (it synchronizes the block).
+//   sumsq = sum_k v_k^2 in binary64: thread t adds the float4 groups g = t, t+256, ...
+//           in increasing order (components in order); the 256 thread sums are combined
+//           by the fixed DPP/readlane tree of wave_sum_f64 per wave, then as
+//           (w0 + w1) + (w2 + w3) over the four waves. The order depends only on K.
+// The w values of the first KEEP groups of each thread (g = tid + 256 i, i < KEEP) are
+// returned in `wk` so the caller can quantize them without re-reading.
+// Must be called by all 256 threads of the block. `slot` (0 or 1) picks the LDS scratch;
+// consecutive calls alternate it, so no barrier is needed after the call (a slot is
+// written again only after every thread has passed the next call's barrier, which
+// follows its reads of the slot).
 // ------------------------------------------------------------------------------------
 struct RowStats {
     float m;
@@ -107,117 +155,89 @@ __device__ __forceinline__ void row_load(const float* __restrict__ u, int K, con
     }
 }
 
-// Statistics from values preloaded by row_load (KEEP > 0, 256 threads) or read here.
-template <int NT, int KEEP>
+// Statistics from values preloaded by row_load (KEEP > 0) or read here.
+template <int KEEP>
 __device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const float* __restrict__ gain, int act,
                                   bool want_sumsq, const float* __restrict__ up,
                                   const float4 (&xa)[KEEP > 0 ? KEEP : 1], const float4 (&gb)[KEEP > 0 ? KEEP : 1],
-                                  float4* wk)
+                                  float4* wk, int slot)
 {
-    static_assert(NT == 64 || NT == 256, "row_stats supports 64- or 256-thread blocks");
-    static_assert(KEEP == 0 || NT == 256, "kept values need one virtual lane per thread");
-    constexpr int V = 256 / NT;
     const int tid = threadIdx.x;
     const int G = K >> 2;
-    double part[V];
+    double s = 0.0;
     float mx = 0.0f;
+    auto visit = [&](float4 a, float4 gv, float4 uv) -> float4 {
+        const float va[4] = {a.x, a.y, a.z, a.w};
+        const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
+        const float ub[4] = {uv.x, uv.y, uv.z, uv.w};
+        float wa[4];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        double s = 0.0;
-        int g = tid + i * NT;
-        auto visit = [&](float4 a, float4 gv, float4 uv) -> float4 {
-            const float va[4] = {a.x, a.y, a.z, a.w};
-            const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
-            const float ub[4] = {uv.x, uv.y, uv.z, uv.w};
-            float wa[4];
+        for (int c = 0; c < 4; ++c) {
+            const float v = act_v(va[c], ub[c], act);
+            if (want_sumsq)
+                s += (double)v * (double)v;
+            wa[c] = gain ? v * ga[c] : v;
+            mx = fmaxf(mx, fabsf(wa[c]));
+        }
+        return make_float4(wa[0], wa[1], wa[2], wa[3]);
+    };
+    int g = tid;
+    if constexpr (KEEP > 0) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float v = act_v(va[c], ub[c], act);
-                if (want_sumsq)
-                    s += (double)v * (double)v;
-                wa[c] = gain ? v * ga[c] : v;
-                mx = fmaxf(mx, fabsf(wa[c]));
-            }
-            return make_float4(wa[0], wa[1], wa[2], wa[3]);
-        };
-        if constexpr (KEEP > 0) {
-#pragma unroll
-            for (int q = 0; q < KEEP; ++q) {
-                if (g + q * 256 < G) {
-                    // gb holds the up values when gated (the gain, a small shared vector, is
-                    // then read here), else the gain
-                    float4 gv = gb[q];
-                    float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-                    if (up) {
-                        uv = gb[q];
-                        gv = gain ? reinterpret_cast<const float4*>(gain)[g + q * 256]
-                                  : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-                    }
-                    wk[q] = visit(xa[q], gv, uv);
+        for (int q = 0; q < KEEP; ++q) {
+            if (g + q * 256 < G) {
+                // gb holds the up values when gated (the gain, a small shared vector, is
+                // then read here), else the gain
+                float4 gv = gb[q];
+                float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                if (up) {
+                    uv = gb[q];
+                    gv = gain ? reinterpret_cast<const float4*>(gain)[g + q * 256]
+                              : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
                 }
+                wk[q] = visit(xa[q], gv, uv);
             }
-            g += KEEP * 256;
         }
-        for (; g < G; g += 256) {
-            const float4 a = reinterpret_cast<const float4*>(u)[g];
-            float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-            float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-            if (gain)
-                gv = reinterpret_cast<const float4*>(gain)[g];
-            if (up)
-                uv = reinterpret_cast<const float4*>(up)[g];
-            visit(a, gv, uv);
-        }
-        part[i] = s;
+        g += KEEP * 256;
     }
-    // max over the block (exact in any order)
-    mx = wave_max(mx);
-    __shared__ float redm[NT / kWave];
-    __shared__ double red[NT / kWave];
+    for (; g < G; g += 256) {
+        const float4 a = reinterpret_cast<const float4*>(u)[g];
+        float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        if (gain)
+            gv = reinterpret_cast<const float4*>(gain)[g];
+        if (up)
+            uv = reinterpret_cast<const float4*>(up)[g];
+        visit(a, gv, uv);
+    }
+    __shared__ float redm[2][4];
+    __shared__ double red[2][4];
     const int wv = tid / kWave;
-    if ((tid & (kWave - 1)) == 0)
-        redm[wv] = mx;
-    double total = 0.0;
-    if (want_sumsq) {
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-#pragma unroll
-            for (int m = 1; m < kWave; m <<= 1)
-                part[i] += __shfl_xor(part[i], m);
-        }
-        // part[i] now holds the sum of virtual wave (wv + i * NT/64)
-        if constexpr (NT == 256) {
-            if ((tid & (kWave - 1)) == 0)
-                red[wv] = part[0];
-        }
+    mx = wave_max(mx);
+    if (want_sumsq)
+        s = wave_sum_f64(s);
+    if ((tid & (kWave - 1)) == 0) {
+        redm[slot][wv] = mx;
+        red[slot][wv] = s;
     }
     __syncthreads();
-    float m = redm[0];
-#pragma unroll
-    for (int w = 1; w < NT / kWave; ++w)
-        m = fmaxf(m, redm[w]);
-    if (want_sumsq) {
-        if constexpr (NT == 256)
-            total = (red[0] + red[1]) + (red[2] + red[3]);
-        else
-            total = (part[0] + part[1]) + (part[2] + part[3]);
-    }
-    __syncthreads();  // LDS scratch may be reused by the caller
+    const float m = fmaxf(fmaxf(redm[slot][0], redm[slot][1]), fmaxf(redm[slot][2], redm[slot][3]));
+    double total = 0.0;
+    if (want_sumsq)
+        total = (red[slot][0] + red[slot][1]) + (red[slot][2] + red[slot][3]);
     return RowStats{m, total};
 }
 
-template <int NT, int KEEP = 0>
+template <int KEEP = 0>
 __device__ RowStats row_stats(const float* __restrict__ u, int K, const float* __restrict__ gain, int act,
-                              bool want_sumsq, const float* __restrict__ up, float4* wk = nullptr)
+                              bool want_sumsq, const float* __restrict__ up, int slot, float4* wk = nullptr)
 {
     float4 xa[KEEP > 0 ? KEEP : 1], gb[KEEP > 0 ? KEEP : 1];
     if constexpr (KEEP > 0)
         row_load<KEEP>(u, K, gain, up, xa, gb);
-    return row_stats_pre<NT, KEEP>(u, K, gain, act, want_sumsq, up, xa, gb, wk);
+    return row_stats_pre<KEEP>(u, K, gain, act, want_sumsq, up, xa, gb, wk, slot);
 }
 
-// Scales of one token from its statistics: s' multiplies w to give the codes; the
-// stored scale s is that of the normalized activation (s' * sqrt(mean v^2 + eps)).
 __device__ __forceinline__ void token_scales(const RowStats& st, int K, bool norm, float eps, float& sp, float& s)
 {
     const float m = st.m < kFloor ? kFloor : st.m;

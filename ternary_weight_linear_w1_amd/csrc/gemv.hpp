@@ -42,6 +42,9 @@ struct FwdArgs {
     int residual;          // 1: Y[t][n] = fl32(Y[t][n] + y[t][n])
 };
 
+constexpr int kBufFlags = 0x00020000;  // buffer descriptor word 3 (gfx9)
+constexpr int kOob = 0x7ffffff0;       // an offset past every buffer: loads give 0, stores drop
+
 // Codes of float4 group g (elements 4g..4g+3) as one little-endian dword (natural order).
 __device__ __forceinline__ uint32_t group_codes(float4 w, float sp)
 {
@@ -49,15 +52,25 @@ __device__ __forceinline__ uint32_t group_codes(float4 w, float sp)
            ((uint32_t)(act_code(w.z, sp) & 0xff) << 16) | ((uint32_t)(act_code(w.w, sp) & 0xff) << 24);
 }
 
-constexpr int kKeep = 8;  // float4 groups per thread kept in VGPRs by the fused prologue
+// float4 groups per thread kept in VGPRs by the fused prologue: enough for the longest
+// row a tile shape serves (L * CPL chunks of 16 groups over 256 threads), at most 8.
+// Kernels start with cold instruction caches, so the unrolled prologue is kept no
+// longer than the row needs.
+template <int L, int CPL>
+constexpr int keep_groups()
+{
+    return (L * CPL + 15) / 16 < 8 ? (L * CPL + 15) / 16 : 8;
+}
 
 // Early loads of token 0 of a tile: the fp32 row (fused) or the int8 codes, issued
 // before the weight loads so that they are not queued behind them.
 constexpr int kPreUnits = 2;  // 16-byte int8 units per thread preloaded (K <= 8192)
+template <int KP>
 struct Pre {
-    float4 xa[kKeep];
-    float4 gb[kKeep];      // gain, or the up values when gated
+    float4 xa[KP];
+    float4 gb[KP];         // gain, or the up values when gated
     uint4 q[kPreUnits];
+    float xs[4];           // per-token scales of the tile (unfused)
 };
 
 __device__ __forceinline__ int64_t x_stride(const FwdArgs& a)
@@ -65,12 +78,12 @@ __device__ __forceinline__ int64_t x_stride(const FwdArgs& a)
     return a.act == 2 ? 2 * (int64_t)a.K : (int64_t)a.K;
 }
 
-template <bool FUSED>
-__device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre& p)
+template <bool FUSED, int KP>
+__device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre<KP>& p)
 {
     if constexpr (FUSED) {
         const float* x = a.X + tok * x_stride(a);
-        row_load<kKeep>(x, a.K, a.gain, a.act == 2 ? x + a.K : nullptr, p.xa, p.gb);
+        row_load<KP>(x, a.K, a.gain, a.act == 2 ? x + a.K : nullptr, p.xa, p.gb);
     } else {
         const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
         const int units = a.K >> 4;
@@ -79,12 +92,20 @@ __device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre
             const int u = (int)threadIdx.x + 256 * i;
             p.q[i] = u < units ? src[u] : make_uint4(0u, 0u, 0u, 0u);
         }
+        // scales through vector loads (tokens past M read 0), so that no scalar-load
+        // wait sits in front of the weight loads
+        const int64_t left = a.M - tok;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.xscale + tok), (short)0, (int)(4 * (left < 4 ? left : 4)), kBufFlags);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            p.xs[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * t, 0, 0));
     }
 }
 
-template <int MT, bool FUSED>
+template <int MT, bool FUSED, int KP>
 __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt, uint4* __restrict__ lds,
-                                            float (&s)[MT], const Pre& pre)
+                                            float (&s)[MT], const Pre<KP>& pre)
 {
     constexpr int NT = 256;
     const int tid = threadIdx.x;
@@ -103,24 +124,24 @@ __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt
             const float* x = a.X + tok * x_stride(a);
             const float* up = a.act == 2 ? x + a.K : nullptr;
             const bool norm = a.gain != nullptr;
-            float4 wk[kKeep];
+            float4 wk[KP];
             RowStats st;
             if (t == 0) {
-                st = row_stats_pre<NT, kKeep>(x, a.K, a.gain, a.act, norm, up, pre.xa, pre.gb, wk);
+                st = row_stats_pre<KP>(x, a.K, a.gain, a.act, norm, up, pre.xa, pre.gb, wk, 0);
             } else {
-                st = row_stats<NT, kKeep>(x, a.K, a.gain, a.act, norm, up, wk);
+                st = row_stats<KP>(x, a.K, a.gain, a.act, norm, up, t & 1, wk);
             }
             float sp;
             token_scales(st, a.K, norm, a.eps, sp, s[t]);
             uint32_t* words = reinterpret_cast<uint32_t*>(dst);
             const int G = a.K >> 2;
 #pragma unroll
-            for (int q = 0; q < kKeep; ++q) {
+            for (int q = 0; q < KP; ++q) {
                 const int g = tid + q * NT;
                 if (g < G)
                     words[g] = group_codes(wk[q], sp);
             }
-            for (int g = tid + kKeep * NT; g < G; g += NT) {
+            for (int g = tid + KP * NT; g < G; g += NT) {
                 const float4 xv = reinterpret_cast<const float4*>(x)[g];
                 float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
                 float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
@@ -140,7 +161,7 @@ __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt
                 words[g] = group_codes(make_float4(wa[0], wa[1], wa[2], wa[3]), sp);
             }
         } else {
-            s[t] = a.xscale[tok];
+            s[t] = pre.xs[t < 4 ? t : 0];
             const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
             int u = tid;
             if (t == 0) {
@@ -175,8 +196,6 @@ __device__ __forceinline__ int group_sum(int v)
     return v;
 }
 
-constexpr int kBufFlags = 0x00020000;  // buffer descriptor word 3 (gfx9)
-constexpr int kOob = 0x7ffffff0;       // an offset past every buffer: loads give 0, stores drop
 
 // L lanes per row, MT tokens per tile, CPL chunks per lane (16*CPL*MT VGPRs of
 // activation codes, CPL*MT <= 8), R rows per lane per pass: R*CPL 16-byte weight loads
@@ -204,7 +223,6 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
     const int KB = a.K >> 2;
     const int64_t N = a.N;
     const int64_t ntiles = (a.M + MT - 1) / MT;
-    const float gamma = *a.gamma;
 
     int woff[R][CPL];
 #pragma unroll
@@ -237,7 +255,10 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
                 w[r][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, woff[r][i], 0, 2));
     };
 
-    for (int64_t tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
+    // The grid has at most as many rows of blocks as there are token tiles, so every block
+    // has a first tile (no entry check: the argument loads can all be issued at once).
+    int64_t tile = blockIdx.y;
+    do {
         const int64_t t0 = tile * MT;
         const int mt = (int)((a.M - t0) < MT ? (a.M - t0) : MT);
         const int64_t pstride = (int64_t)gridDim.x * RPP;
@@ -252,8 +273,12 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
 
         // Activations of token 0 first, then the first two passes of weights, then the
         // prologue arithmetic while the weights are in flight.
-        Pre pre;
+        Pre<keep_groups<L, CPL>()> pre;
         stage_preload<FUSED>(a, t0, pre);
+        // gamma through a vector load as well, ahead of the weights
+        const float gamma = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       __builtin_amdgcn_make_buffer_rsrc((void*)a.gamma, (short)0, 4, kBufFlags), 0, 0, 0));
         u32x4 cur[R][CPL], nxt[R][CPL];
         float ycur[R][MT], ynxt[R][MT];
         load_pass(rb, cur, ycur, ry, mt);
@@ -366,7 +391,8 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
             compute_pass(rb + pstride, nxt, ynxt);
             load_pass(rb + 3 * pstride, nxt, ynxt, ry, mt);
         }
-    }
+        tile += gridDim.y;
+    } while (tile < ntiles);
 }
 
 // Any K % 4 == 0 and any alignment of the packed rows: byte loads, one wave per row,
@@ -381,6 +407,7 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(FwdArgs a)
     const int64_t ntiles = (a.M + MT - 1) / MT;
     const float gamma = *a.gamma;
     const bool norm = a.gain != nullptr;
+    int calls = 0;  // statistics calls so far: their LDS slots alternate
     for (int64_t tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
         const int64_t t0 = tile * MT;
         const int mt = (int)((a.M - t0) < MT ? (a.M - t0) : MT);
@@ -392,7 +419,8 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(FwdArgs a)
             if (t < mt) {
                 if constexpr (FUSED) {
                     const float* x = a.X + (t0 + t) * x_stride(a);
-                    const RowStats st = row_stats<256>(x, a.K, a.gain, a.act, norm, a.act == 2 ? x + a.K : nullptr);
+                    const RowStats st =
+                        row_stats(x, a.K, a.gain, a.act, norm, a.act == 2 ? x + a.K : nullptr, calls++ & 1);
                     token_scales(st, a.K, norm, a.eps, sp[t], s);
                 } else {
                     s = a.xscale[t0 + t];

@@ -27,12 +27,13 @@ struct QuantArgs {
 // row is re-read (it is L2-resident after pass 1).
 __global__ __launch_bounds__(256) void quantize_act_kernel(QuantArgs a)
 {
+    int calls = 0;  // statistics calls so far: their LDS slots alternate
     for (int64_t t = blockIdx.x; t < a.M; t += gridDim.x) {
         const int64_t stride = a.act == 2 ? 2 * (int64_t)a.K : (int64_t)a.K;
         const float* u = a.X + t * stride;
         const float* up = a.act == 2 ? u + a.K : nullptr;
         const bool norm = a.gain != nullptr;
-        const RowStats st = row_stats<256>(u, a.K, a.gain, a.act, norm, up);
+        const RowStats st = row_stats(u, a.K, a.gain, a.act, norm, up, calls++ & 1);
         float sp, s;
         token_scales(st, a.K, norm, a.eps, sp, s);
         if (threadIdx.x == 0)
