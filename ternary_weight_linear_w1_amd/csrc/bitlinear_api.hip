@@ -100,7 +100,8 @@ void launch_k64(const bl::FwdArgs& a, int wg_per_cu, hipStream_t stream)
     const int64_t max_x = int64_t(cu_count()) * wg_per_cu;
     const int gx = (int)(passes < max_x ? passes : max_x);
     const int gy = (int)(tiles < 65535 ? tiles : 65535);
-    const size_t lds = (size_t)MT * (size_t)a.K;
+    // pre-quantized codes with L >= 64 go straight to registers (no LDS staging)
+    const size_t lds = (!FUSED && L >= 64) ? 0 : (size_t)MT * (size_t)a.K;
     if (a.residual) {
         // (the row loop strides by the grid, so any grid width is correct)
         if constexpr (MT * R <= 4)
@@ -122,12 +123,22 @@ bool dispatch_mt1(const bl::FwdArgs& a, hipStream_t stream)
     if (KC <= 48) { launch_k64<16, 1, 3, 1, FUSED>(a, 2, stream); return true; }
     if (KC <= 64) { launch_k64<16, 1, 4, 1, FUSED>(a, 2, stream); return true; }
     if (KC <= 128) {
-        if (big) launch_k64<32, 1, 4, 2, FUSED>(a, 2, stream);
-        else launch_k64<32, 1, 4, 1, FUSED>(a, 1, stream);
+        if (!big)
+            launch_k64<32, 1, 4, 1, FUSED>(a, 1, stream);
+        else if constexpr (FUSED)
+            launch_k64<32, 1, 4, 2, FUSED>(a, 2, stream);
+        else  // one row per lane and more blocks keep the HBM queue fuller on long matrices
+            launch_k64<32, 1, 4, 1, FUSED>(a, a.N * (int64_t)a.K >= (int64_t(128) << 20) ? 3 : 2, stream);
         return true;
     }
     if (KC <= 256) { launch_k64<64, 1, 4, 1, FUSED>(a, 2, stream); return true; }
-    if (KC <= 512) { launch_k64<128, 1, 4, 2, FUSED>(a, 1, stream); return true; }
+    if (KC <= 512) {
+        if constexpr (FUSED)
+            launch_k64<128, 1, 4, 2, FUSED>(a, 1, stream);
+        else
+            launch_k64<256, 1, 2, 2, FUSED>(a, 3, stream);  // codes straight to registers
+        return true;
+    }
     if (KC <= 1024) { launch_k64<256, 1, 4, 1, FUSED>(a, 2, stream); return true; }
     return false;
 }

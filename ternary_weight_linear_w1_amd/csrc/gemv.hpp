@@ -78,19 +78,21 @@ __device__ __forceinline__ int64_t x_stride(const FwdArgs& a)
     return a.act == 2 ? 2 * (int64_t)a.K : (int64_t)a.K;
 }
 
-template <bool FUSED, int KP>
+template <bool FUSED, bool STAGE, int KP>
 __device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre<KP>& p)
 {
     if constexpr (FUSED) {
         const float* x = a.X + tok * x_stride(a);
         row_load<KP>(x, a.K, a.gain, a.act == 2 ? x + a.K : nullptr, p.xa, p.gb);
     } else {
-        const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
-        const int units = a.K >> 4;
+        if constexpr (STAGE) {
+            const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
+            const int units = a.K >> 4;
 #pragma unroll
-        for (int i = 0; i < kPreUnits; ++i) {
-            const int u = (int)threadIdx.x + 256 * i;
-            p.q[i] = u < units ? src[u] : make_uint4(0u, 0u, 0u, 0u);
+            for (int i = 0; i < kPreUnits; ++i) {
+                const int u = (int)threadIdx.x + 256 * i;
+                p.q[i] = u < units ? src[u] : make_uint4(0u, 0u, 0u, 0u);
+            }
         }
         // scales through vector loads (tokens past M read 0), so that no scalar-load
         // wait sits in front of the weight loads
@@ -205,7 +207,10 @@ __device__ __forceinline__ int group_sum(int v)
 // the end (hardware zero-fill / dropped store), so the loop has no branches and the
 // outstanding-load counts stay exact. With RES the old outputs of a pass are loaded
 // just before its weights (in-order completion: waiting for the weights covers them)
-// and the product is added to them.
+// and the product is added to them. Pre-quantized codes are staged once per block in
+// LDS when many row groups share them (L < 64); with L >= 64 (at most four row groups)
+// each lane loads its own chunks into registers ahead of its weights, which skips the
+// staging and its barriers.
 template <int L, int MT, int CPL, int R, bool FUSED, bool RES>
 __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
 {
@@ -273,8 +278,31 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
 
         // Activations of token 0 first, then the first two passes of weights, then the
         // prologue arithmetic while the weights are in flight.
+        constexpr bool DIRECT = !FUSED && L >= 64;
         Pre<keep_groups<L, CPL>()> pre;
-        stage_preload<FUSED>(a, t0, pre);
+        stage_preload<FUSED, !DIRECT>(a, t0, pre);
+        uint32_t act[MT][CPL][16];
+        if constexpr (DIRECT) {
+            // tokens past M and chunks past K read as zero
+            const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(a.Xq + t0 * (int64_t)a.K), (short)0, (int)(mt * a.K), kBufFlags);
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int c = j + i * L;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const u32x4 v = __builtin_bit_cast(
+                            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       rx, c < KC ? t * a.K + c * 64 + 16 * d : kOob, 0, 0));
+                        act[t][i][4 * d + 0] = v.x;
+                        act[t][i][4 * d + 1] = v.y;
+                        act[t][i][4 * d + 2] = v.z;
+                        act[t][i][4 * d + 3] = v.w;
+                    }
+                }
+        }
         // gamma through a vector load as well, ahead of the weights
         const float gamma = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -285,11 +313,16 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
         load_pass(rb + pstride, nxt, ynxt, ry, mt);
 
         float s[MT];
-        __syncthreads();  // LDS of the previous tile is no longer read
-        stage_codes<MT, FUSED>(a, t0, mt, lds_codes, s, pre);
-        __syncthreads();
+        if constexpr (DIRECT) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                s[t] = t < mt ? pre.xs[t] : 1.0f;
+        } else {
+            __syncthreads();  // LDS of the previous tile is no longer read
+            stage_codes<MT, FUSED>(a, t0, mt, lds_codes, s, pre);
+            __syncthreads();
+        }
 
-        uint32_t act[MT][CPL][16];
         int32_t xs[MT];
         float csc[MT];
 #pragma unroll
@@ -302,7 +335,10 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                    if (c < KC)
+                    if constexpr (DIRECT)
+                        v = make_uint4(act[t][i][4 * d + 0], act[t][i][4 * d + 1], act[t][i][4 * d + 2],
+                                       act[t][i][4 * d + 3]);
+                    else if (c < KC)
                         v = src[4 * c + d];
                     uint32_t o[4];
                     transpose_bytes(v.x, v.y, v.z, v.w, o);
@@ -323,9 +359,14 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
             int32_t accv[R][MT];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
+                // four independent accumulators (one per dword of a chunk) keep the dot4
+                // chain short; integer addition makes the split exact
+                int32_t part[MT][4];
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    accv[r][t] = 0;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        part[t][d] = 0;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
                     const uint32_t wd[4] = {w[r][i].x, w[r][i].y, w[r][i].z, w[r][i].w};
@@ -336,13 +377,13 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
                             const uint32_t u = (wd[d] >> (2 * f)) & 0x03030303u;
 #pragma unroll
                             for (int t = 0; t < MT; ++t)
-                                accv[r][t] = __builtin_amdgcn_sdot4((int)u, (int)act[t][i][4 * d + f], accv[r][t], false);
+                                part[t][d] = __builtin_amdgcn_sdot4((int)u, (int)act[t][i][4 * d + f], part[t][d], false);
                         }
                     }
                 }
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    accv[r][t] = group_sum<(L < 64 ? L : 64)>(accv[r][t] - xs[t]);
+                    accv[r][t] = group_sum<(L < 64 ? L : 64)>(((part[t][0] + part[t][1]) + (part[t][2] + part[t][3])) - xs[t]);
             }
             if constexpr (L > 64) {
                 if ((tid & 63) == 0) {

@@ -110,3 +110,11 @@ def test_100b_decode_m1(i):
 def test_100b_small_batch_m64(i):
     name, N, K, mode = LAYER_100B[i]
     check_matrix(5, i + 64, N, K, mode, 64, fused=False, sampled=True)
+
+
+@pytest.mark.parametrize("i", range(4))
+def test_100b_decode_m1_prequantized(i):
+    """The two-call path (quantize, then the product) at M = 1, full outputs and
+    accumulators: the launch shapes the pre-quantized dispatch picks for long rows."""
+    name, N, K, mode = LAYER_100B[i]
+    check_matrix(5, i + 16, N, K, mode, 1, fused=False)
