@@ -51,6 +51,12 @@ def lib():
         L.ora_pack.restype = None
         L.ora_unpack.argtypes = [vp, i64, i64, vp]
         L.ora_unpack.restype = i64
+        L.ora_pack5_row_bytes.argtypes = [i64]
+        L.ora_pack5_row_bytes.restype = i64
+        L.ora_pack5.argtypes = [vp, i64, i64, vp]
+        L.ora_pack5.restype = None
+        L.ora_unpack5.argtypes = [vp, i64, i64, vp]
+        L.ora_unpack5.restype = i64
         L.ora_quantize_act.argtypes = [vp, i64, i64, vp, vp]
         L.ora_quantize_act.restype = None
         L.ora_quantize_act_norm.argtypes = [vp, i64, i64, vp, f32, ctypes.c_int, vp, vp, vp]
@@ -104,6 +110,30 @@ def unpack(packed: np.ndarray, k: int):
     n = packed.shape[0]
     q = np.empty((n, k), dtype=np.int8)
     bad = lib().ora_unpack(_ptr(packed), n, k, _ptr(q))
+    return q, int(bad)
+
+
+def pack5_row_bytes(k: int) -> int:
+    return int(lib().ora_pack5_row_bytes(int(k)))
+
+
+def pack5(q: np.ndarray) -> np.ndarray:
+    """Codes int8 [N][K] -> five codes per byte, uint8 [N][16 * ceil(K/80)] (O3b in the C file)."""
+    q = _c(q, np.int8)
+    n, k = q.shape
+    out = np.empty((n, pack5_row_bytes(k)), dtype=np.uint8)
+    lib().ora_pack5(_ptr(q), n, k, _ptr(out))
+    return out
+
+
+def unpack5(packed: np.ndarray, k: int):
+    """Returns (codes int8 [N][K], number of invalid bytes or non-zero padding digits)."""
+    packed = _c(packed, np.uint8)
+    n = packed.shape[0]
+    if packed.shape[1] != pack5_row_bytes(k):
+        raise ValueError("row length must be 16 * ceil(K/80)")
+    q = np.empty((n, k), dtype=np.int8)
+    bad = lib().ora_unpack5(_ptr(packed), n, k, _ptr(q))
     return q, int(bad)
 
 

@@ -132,6 +132,64 @@ int64_t ora_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* q)
 }
 
 /* ---------------------------------------------------------------------------------
+ * O3b packing, five codes per byte (1.6 bits per weight): the denser alternative to
+ *     the 2-bit fields ([P1] s.3: several trits in one 8-bit integer; [P5] s.2.1: a
+ *     2-bit field wastes one of its four states, and more compact encodings exist).
+ *     3^5 = 243 <= 256, so five base-3 digits fit in a byte.
+ *     Byte j of row n holds codes k = 5j .. 5j+4 as the base-3 number
+ *         sum_{i=0..4} (q[n][5j+i] + 1) * 3^i          (digit i = code 5j+i, plus one)
+ *     with q = 0 for k >= K. Rows are 16 * ceil(K/80) bytes long (whole 16-byte
+ *     chunks of 80 codes); bytes past the last group of the row encode five zero
+ *     codes (value 121).
+ * ------------------------------------------------------------------------------- */
+int64_t ora_pack5_row_bytes(int64_t K)
+{
+    return 16 * ((K + 79) / 80);
+}
+
+void ora_pack5(const int8_t* q, int64_t N, int64_t K, uint8_t* packed)
+{
+    int64_t rb = ora_pack5_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < rb; ++j) {
+            unsigned value = 0, weight = 1;
+            for (int i = 0; i < 5; ++i) {
+                int64_t k = 5 * j + i;
+                int code = k < K ? q[n * K + k] : 0;
+                value += (unsigned)(code + 1) * weight;
+                weight *= 3u;
+            }
+            packed[n * rb + j] = (uint8_t)value;
+        }
+    }
+}
+
+/* Inverse of ora_pack5 on the first K codes of each row. Returns the number of bytes
+ * above 242 (never produced by the packer) plus the number of digits past K that are
+ * not the zero code; such bytes still decode digit by digit. */
+int64_t ora_unpack5(const uint8_t* packed, int64_t N, int64_t K, int8_t* q)
+{
+    int64_t rb = ora_pack5_row_bytes(K), bad = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < rb; ++j) {
+            unsigned value = packed[n * rb + j];
+            if (value > 242u)
+                ++bad;
+            for (int i = 0; i < 5; ++i) {
+                int64_t k = 5 * j + i;
+                int code = (int)(value % 3u) - 1;
+                value /= 3u;
+                if (k < K)
+                    q[n * K + k] = (int8_t)code;
+                else if (code != 0)
+                    ++bad;
+            }
+        }
+    }
+    return bad;
+}
+
+/* ---------------------------------------------------------------------------------
  * O4  per-token absmax int8 activation quantization
  *     ([P1] s.1, [P3], [P4] s.2: absmax taken per token; [P5] s.2.2: scale
  *     127 / max(|x|, 1e-8), round, clamp to [-128, 127]).

@@ -430,3 +430,49 @@ def test_decode_layer_matches_dense_fp64_of_dequantized_operands(ora):
     assert close(mid["h1"], h.astype(np.float64) + d_o, np.abs(d_o).max())
     d_d = dense(mid["u"], "down", gains["g_ffn"], 1)
     assert close(h2, mid["h1"].astype(np.float64) + d_d, np.abs(d_d).max())
+
+
+# ----------------------------------------------------------------------------- 5 codes per byte
+
+def test_pack5_golden(ora, golden):
+    g = golden["pack5_order"]
+    q = np.array(g["codes"], np.int8)
+    packed = ora.pack5(q)
+    assert packed.tolist() == g["packed"]
+    back, bad = ora.unpack5(packed, q.shape[1])
+    assert bad == 0 and (back == q).all()
+
+
+def test_pack5_is_the_base3_numeral_of_every_pattern(ora):
+    """All 3^5 five-code groups: the byte equals the base-3 numeral of the digits (code + 1,
+    first code least significant) as Python's int(., 3) parses it, and the 243 bytes are
+    distinct, i.e. the code is a bijection onto 0..242."""
+    import itertools
+    pats = np.array(list(itertools.product((-1, 0, 1), repeat=5)), np.int8)    # [243][5]
+    packed = ora.pack5(pats.reshape(1, -1))[0, :243]
+    for pat, byte in zip(pats, packed):
+        numeral = "".join(str(c + 1) for c in pat[::-1])
+        assert int(byte) == int(numeral, 3)
+    assert sorted(packed.tolist()) == list(range(243))
+
+
+@pytest.mark.parametrize("K", [1, 4, 5, 79, 80, 81, 2560, 6912])
+def test_pack5_round_trip_and_row_length(ora, K):
+    q = ora.weight_codes(datagen.gg_weights(7, K, 600 + K), np.float32(0.02))
+    packed = ora.pack5(q)
+    assert packed.shape == (7, 16 * ((K + 79) // 80))
+    assert packed.max() <= 242
+    back, bad = ora.unpack5(packed, K)
+    assert bad == 0 and (back == q).all()
+    # bytes past the last five-code group encode five zero codes
+    assert (packed[:, (K + 4) // 5:] == 121).all()
+    # 1.6 bits per weight instead of 2 (plus at most one 16-byte chunk per row)
+    assert packed.shape[1] <= (K * 2 // 8) * 0.8 + 16
+
+
+def test_unpack5_flags_invalid_bytes_and_padding(ora):
+    packed = np.full((1, 16), 121, np.uint8)
+    packed[0, 1] = 243                    # above the largest numeral (codes 5..9, inside K)
+    packed[0, 2] = 0                      # covers codes 10..14: 12..14 lie past K = 12
+    _, bad = ora.unpack5(packed, 12)
+    assert bad == 1 + 3
