@@ -149,6 +149,32 @@ int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const f
                                    int act, const uint8_t* W_packed, const float* gamma, int64_t N,
                                    float* Y, hipStream_t stream);
 
+/*
+ * Five ternary codes per byte (1.6 bits per weight) instead of four: "微软AI大模型炸场"
+ * s.3 packs several trits into one 8-bit integer, and "BitNet b1.58 深度解析" s.2.1 notes
+ * that a 2-bit field leaves one of its four states unused; 3^5 = 243 <= 256.
+ *
+ * Format: byte j of row n is the base-3 numeral sum_{i=0..4} (q[n][5j+i] + 1) * 3^i
+ * (first code least significant; q = 0 past K). A row is
+ * bitlinear_packed5_row_bytes(K) = 16 * ceil(K / 80) bytes; bytes past the row's codes
+ * encode five zero codes (121). gamma is the one bitlinear_pack_weights computes.
+ *
+ * bitlinear_packed5_row_bytes returns 0 for an invalid K.
+ *
+ * bitlinear_repack5 converts bitlinear_pack_weights' 2-bit layout W_packed [N][K/4] into
+ * this one, W_packed5 [N][row bytes] (4-byte aligned, written; must not overlap W_packed).
+ *
+ * bitlinear_forward5 is bitlinear_forward on W_packed5: the same exact int32 sums and
+ * the same rescale, y[t][n] = fl32(fl32(acc[t][n]) * fl32(gamma / s_t)). K must be a
+ * multiple of 16 and at most 131072 (a token's codes are staged in LDS), N at most
+ * 2^27; Xq and W_packed5 16-byte aligned. A byte above
+ * 242 (never written by the packer) gives unspecified results.
+ */
+int64_t bitlinear_packed5_row_bytes(int64_t K);
+int bitlinear_repack5(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W_packed5, hipStream_t stream);
+int bitlinear_forward5(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed5,
+                       const float* gamma, int64_t N, float* Y, int32_t* acc, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,9 @@ EXPORTED = (
     "bitlinear_forward_f32",
     "bitlinear_forward_residual",
     "bitlinear_forward_f32_residual",
+    "bitlinear_packed5_row_bytes",
+    "bitlinear_repack5",
+    "bitlinear_forward5",
 )
 
 _lib = None
@@ -64,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward_residual.restype = ci
         L.bitlinear_forward_f32_residual.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, i64, vp, vp]
         L.bitlinear_forward_f32_residual.restype = ci
+        L.bitlinear_packed5_row_bytes.argtypes = [i64]
+        L.bitlinear_packed5_row_bytes.restype = i64
+        L.bitlinear_repack5.argtypes = [vp, i64, i64, vp, vp]
+        L.bitlinear_repack5.restype = ci
+        L.bitlinear_forward5.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp]
+        L.bitlinear_forward5.restype = ci
         _lib = L
     return _lib
 
@@ -220,3 +229,45 @@ def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=
     _check(fn(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(W_packed), _ptr(gamma), N, _ptr(y), _stream(stream)),
            name)
     return y
+
+
+def bitlinear_packed5_row_bytes(K: int) -> int:
+    """Bytes per row of the five-codes-per-byte format: 16 * ceil(K / 80)."""
+    return int(lib().bitlinear_packed5_row_bytes(int(K)))
+
+
+def bitlinear_repack5(W_packed, out=None, stream=None):
+    """2-bit packed weights [N][K/4] -> five codes per byte [N][16 * ceil(K/80)]."""
+    import torch
+    _need(W_packed, torch.uint8, "W_packed", 2)
+    N, K = W_packed.shape[0], W_packed.shape[1] * 4
+    rb = bitlinear_packed5_row_bytes(K)
+    if out is None:
+        out = torch.empty((N, rb), dtype=torch.uint8, device=W_packed.device)
+    _need(out, torch.uint8, "out", shape=(N, rb))
+    _check(lib().bitlinear_repack5(_ptr(W_packed), N, K, _ptr(out), _stream(stream)), "bitlinear_repack5")
+    return out
+
+
+def bitlinear_forward5(Xq, x_scale, W_packed5, gamma, y=None, acc=None, stream=None):
+    """bitlinear_forward on weights packed five codes per byte."""
+    import torch
+    _need(Xq, torch.int8, "Xq", 2)
+    _need(W_packed5, torch.uint8, "W_packed5", 2)
+    M, K = Xq.shape
+    N = W_packed5.shape[0]
+    if W_packed5.shape[1] != bitlinear_packed5_row_bytes(K):
+        raise ValueError("W_packed5 must have 16 * ceil(K/80) columns")
+    _need(x_scale, torch.float32, "x_scale", shape=(M,))
+    _need(gamma, torch.float32, "gamma", shape=(1,))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    _need(y, torch.float32, "y", shape=(M, N))
+    if acc is True:
+        acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    if isinstance(acc, torch.Tensor):
+        _need(acc, torch.int32, "acc", shape=(M, N))
+    _check(lib().bitlinear_forward5(_ptr(Xq), _ptr(x_scale), M, K, _ptr(W_packed5), _ptr(gamma), N, _ptr(y),
+                                    _ptr(acc if isinstance(acc, torch.Tensor) else None), _stream(stream)),
+           "bitlinear_forward5")
+    return (y, acc) if isinstance(acc, torch.Tensor) else y

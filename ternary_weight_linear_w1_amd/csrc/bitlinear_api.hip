@@ -11,6 +11,7 @@
 #include "device_common.hpp"
 #include "gemm.hpp"
 #include "gemv.hpp"
+#include "gemv5.hpp"
 #include "pack.hpp"
 #include "quant.hpp"
 
@@ -307,6 +308,56 @@ int forward_f32_impl(const float* X, int64_t M, int64_t K, const float* gain, fl
     return launched();
 }
 
+
+// ---------------------------------------------------------------------- five codes per byte
+
+int64_t row_bytes5(int64_t K)
+{
+    return 16 * ((K + 79) / 80);
+}
+
+template <int L, int MT, int CPL>
+void launch5(const bl::Fwd5Args& a, hipStream_t stream)
+{
+    constexpr int RG = 256 / L;
+    const int64_t passes = (a.N + RG - 1) / RG;
+    const int64_t tiles = (a.M + MT - 1) / MT;
+    const int64_t max_x = int64_t(cu_count()) * 2;
+    const int gx = (int)(passes < max_x ? passes : max_x);
+    const int gy = (int)(tiles < 65535 ? tiles : 65535);
+    const size_t lds = (size_t)MT * (size_t)(a.RB >> 4) * 80;
+    hipLaunchKernelGGL((bl::gemv5_kernel<L, MT, CPL>), dim3(gx, gy), dim3(256), lds, stream, a);
+}
+
+// Lanes per row: the fewest (16 .. 256) whose chunks cover a row; tiles of 1, 2 or 4
+// tokens as long as the staged codes fit in LDS.
+template <int MT, int CPL>
+bool dispatch5_mt(const bl::Fwd5Args& a, hipStream_t stream)
+{
+    const int KC = a.RB >> 4;
+    if (KC <= 16 * CPL) { launch5<16, MT, CPL>(a, stream); return true; }
+    if (KC <= 32 * CPL) { launch5<32, MT, CPL>(a, stream); return true; }
+    if (KC <= 64 * CPL) { launch5<64, MT, CPL>(a, stream); return true; }
+    if (KC <= 128 * CPL) { launch5<128, MT, CPL>(a, stream); return true; }
+    if (KC <= 256 * CPL) { launch5<256, MT, CPL>(a, stream); return true; }
+    return false;
+}
+
+void dispatch5(const bl::Fwd5Args& a, hipStream_t stream)
+{
+    const int64_t staged = (int64_t)(a.RB >> 4) * 80;    // LDS bytes per token
+    constexpr int64_t kLdsBudget = 144 * 1024;
+    // fewer chunks per lane for multi-token tiles: the rearranged activations of every
+    // token stay in registers
+    if (a.M >= 3 && 4 * staged <= kLdsBudget && dispatch5_mt<4, 1>(a, stream))
+        return;
+    if (a.M >= 2 && 2 * staged <= kLdsBudget && dispatch5_mt<2, 2>(a, stream))
+        return;
+    if (dispatch5_mt<1, 4>(a, stream))
+        return;
+    launch5<256, 1, 8>(a, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -422,6 +473,63 @@ int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const f
                                    hipStream_t stream)
 {
     return forward_f32_impl(X, M, K, gain, eps, act, W_packed, gamma, N, Y, 1, stream);
+}
+
+int64_t bitlinear_packed5_row_bytes(int64_t K)
+{
+    if (K < 4 || K > BITLINEAR_MAX_K || (K % 4) != 0)
+        return 0;
+    return row_bytes5(K);
+}
+
+int bitlinear_repack5(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W_packed5, hipStream_t stream)
+{
+    if (!W_packed || !W_packed5)
+        return BITLINEAR_ERR_NULL;
+    int st = check_nk(N, K);
+    if (st != BITLINEAR_OK)
+        return st;
+    const int64_t rb = row_bytes5(K);
+    if (!aligned(W_packed5, 4))
+        return BITLINEAR_ERR_ALIGN;
+    if (overlap(W_packed5, N * rb, W_packed, N * (K / 4)))
+        return BITLINEAR_ERR_ALIAS;
+    const int64_t total = N * (rb / 4);
+    const int64_t blocks = (total + 255) / 256;
+    const int64_t cap = int64_t(cu_count()) * 8;
+    hipLaunchKernelGGL(bl::repack5_kernel, dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(256), 0, stream,
+                       W_packed, N, (int)K, W_packed5, (int)rb);
+    return launched();
+}
+
+int bitlinear_forward5(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed5,
+                       const float* gamma, int64_t N, float* Y, int32_t* acc, hipStream_t stream)
+{
+    if (!Xq || !x_scale || !W_packed5 || !gamma || !Y)
+        return BITLINEAR_ERR_NULL;
+    int st = check_mk(M, K);
+    if (st != BITLINEAR_OK)
+        return st;
+    if ((st = check_nk(N, K)) != BITLINEAR_OK)
+        return st;
+    // a staged row of codes must fit in LDS (and the widest tile covers 2048 chunks)
+    if ((K % 16) != 0 || K > 131072 || M > kMaxElems / N || N > (int64_t(1) << 27))
+        return BITLINEAR_ERR_SHAPE;
+    if (!aligned(Xq, 16) || !aligned(x_scale, 4) || !aligned(W_packed5, 16) || !aligned(gamma, 4) ||
+        !aligned(Y, 4) || (acc && !aligned(acc, 4)))
+        return BITLINEAR_ERR_ALIGN;
+    const int64_t rb = row_bytes5(K);
+    const int64_t ybytes = M * N * 4;
+    const void* ins[4] = {Xq, x_scale, W_packed5, gamma};
+    const int64_t insz[4] = {M * K, M * 4, N * rb, 4};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(Y, ybytes, ins[i], insz[i]) || overlap(acc, ybytes, ins[i], insz[i]))
+            return BITLINEAR_ERR_ALIAS;
+    if (overlap(Y, ybytes, acc, ybytes))
+        return BITLINEAR_ERR_ALIAS;
+    bl::Fwd5Args a{Xq, x_scale, W_packed5, gamma, Y, acc, M, N, (int)K, (int)rb};
+    dispatch5(a, stream);
+    return launched();
 }
 
 }  // extern "C"

@@ -143,3 +143,28 @@ def test_binding_without_gpu_fails_loudly():
     w = torch.zeros((4, 8))
     with pytest.raises(ValueError):
         bl.bitlinear_pack_weights(w)
+
+
+def test_packed5_row_bytes(L):
+    f = L.bitlinear_packed5_row_bytes
+    assert f(2560) == 512 and f(6912) == 1392 and f(8192) == 1648 and f(80) == 16 and f(84) == 32
+    assert f(0) == 0 and f(6) == 0
+
+
+def test_five_per_byte_calls_reject_before_launch(L):
+    a = 1 << 20
+    r = L.bitlinear_repack5
+    assert r(None, 8, 64, P(2 * a), None) == ERR_NULL
+    assert r(P(a), 8, 66, P(2 * a), None) == ERR_SHAPE
+    assert r(P(a), 8, 64, P(2 * a + 2), None) == ERR_ALIGN
+    assert r(P(a), 8, 64, P(a + 64), None) == ERR_ALIAS
+    f = L.bitlinear_forward5
+    args = lambda **kw: [kw.get("Xq", P(a)), kw.get("s", P(2 * a)), kw.get("M", 1), kw.get("K", 64),
+                         kw.get("W", P(3 * a)), kw.get("g", P(4 * a)), kw.get("N", 8), kw.get("Y", P(5 * a)),
+                         kw.get("acc", None), None]
+    assert f(*args(W=None)) == ERR_NULL
+    assert f(*args(K=68)) == ERR_SHAPE                 # K % 16 != 0
+    assert f(*args(K=131072 + 16)) == ERR_SHAPE        # a token's codes no longer fit in LDS
+    assert f(*args(Xq=P(a + 4))) == ERR_ALIGN
+    assert f(*args(W=P(3 * a + 4))) == ERR_ALIGN
+    assert f(*args(Y=P(3 * a))) == ERR_ALIAS
