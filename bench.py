@@ -452,6 +452,9 @@ def run_extra(torch, bl, datagen, dev, mats2b):
             del m
         res["2B_prefill_M%d" % M] = r
         log("extra prefill M=%d: %s" % (M, r))
+    # ---- five codes per byte (1.6 bits per weight) against the 2-bit fields, pre-quantized
+    res["trits5_vs_2bit"] = run_trits5(torch, bl, datagen, dev)
+    torch.cuda.empty_cache()
     # ---- decode stack: 30 layers of the 2B shapes at M = 1, plain and gated FFN
     for gated in (False, True):
         res["2B_stack30_M1" + ("_gated" if gated else "")] = run_stack(torch, bl, datagen, dev, gated)
@@ -468,6 +471,34 @@ def run_extra(torch, bl, datagen, dev, mats2b):
     del w, packed, ws
     torch.cuda.empty_cache()
     return res
+
+
+def run_trits5(torch, bl, datagen, dev):
+    """bitlinear_forward5 (five codes per byte) next to bitlinear_forward on the same
+    weights and codes, M = 1 and 8, 2B and 100B shapes, rotating weight copies."""
+    out = {}
+    for tag, N, K in (("2B_up", 6912, 2560), ("2B_down", 2560, 6912), ("100B_up", 28672, 8192),
+                      ("100B_down", 8192, 28672)):
+        w = datagen.gg_weights_torch(N, K, datagen.stream_id(7, 0, 0, 0), dev)
+        packed, gamma = bl.bitlinear_pack_weights(w)
+        del w
+        p5 = bl.bitlinear_repack5(packed)
+        C = n_copies(N * K // 4)
+        c2 = [packed] + [packed.clone() for _ in range(C - 1)]
+        c5 = [p5] + [p5.clone() for _ in range(C - 1)]
+        for M in (1, 8):
+            x = datagen.outlier_acts_torch(M, K, datagen.stream_id(7, 1, M, 1), dev)
+            xq, s = bl.bitlinear_quantize_act(x)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            t2 = time_kernel(torch, lambda c: bl.bitlinear_forward(xq, s, c2[c], gamma, y=y), C, 100)
+            t5 = time_kernel(torch, lambda c: bl.bitlinear_forward5(xq, s, c5[c], gamma, y=y), C, 100)
+            out["%s_M%d" % (tag, M)] = {"us_2bit": round(t2 * 1e6, 2), "us_1.6bit": round(t5 * 1e6, 2),
+                                        "MB_2bit": round(N * K / 4 / 1e6, 2), "MB_1.6bit": round(p5.numel() / 1e6, 2),
+                                        "speedup_1.6bit": round(t2 / t5, 3)}
+        del c2, c5
+        torch.cuda.empty_cache()
+    log("extra trits5: %s" % out)
+    return out
 
 
 STACK_DIMS = dict(hidden=2560, heads=20, kv_heads=5, head_dim=128, ffn=6912)
