@@ -23,7 +23,9 @@ Also printed in the same JSON line:
 Other modes:
   --profile roofline   only the dominant kernel plus a copy kernel of known size
                        (for rocprofv3 --pmc runs);
-  --summarize-pmc F W  turn two rocprofv3 counter CSVs into profiles/ text.
+  --summarize-pmc F W  turn two rocprofv3 counter CSVs into profiles/ text;
+  --summarize-trace T S OUT  turn a rocprofv3 kernel trace and its stats CSV into a
+                       profiles/ text (per kernel and grid: calls, average, median, min).
 """
 from __future__ import annotations
 
@@ -191,6 +193,44 @@ def read_traffic():
         return None
 
 
+def summarize_trace(trace_csv, stats_csv, out, command=None):
+    """Per (kernel, grid) durations from a rocprofv3 kernel trace (End - Start per
+    dispatch) and the library rows of its stats table, as text for profiles/."""
+    import csv
+    import statistics
+    rows = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "bl::" not in name:
+                continue
+            short = name.replace("void ", "").split("(")[0]
+            key = (short, int(r.get("Grid_Size_X", r.get("Grid_Size", 0))) // 256, int(r.get("Grid_Size_Y", 1)),
+                   r.get("VGPR_Count", r.get("Arch_VGPR_Count", "")), r.get("LDS_Block_Size", r.get("LDS_Size", "")))
+            rows.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    with open(out, "w") as f:
+        f.write("# rocprofv3 kernel trace of bench.py (library kernels; durations End - Start per dispatch, us)\n")
+        f.write("# command (GPU box, repository root in $R):\n")
+        f.write("#   cd /tmp && rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof_bench -o trace "
+                "--output-format csv -- python3 $R/bench.py --steps 80 --warmup 8 --no-extra --no-cpu-baseline\n")
+        f.write("#   python3 bench.py --summarize-trace <trace_kernel_trace.csv> <trace_kernel_stats.csv> <this file>\n")
+        f.write("# WGs = grid X / 256 (work-groups per launch row), gridY = token tiles\n#\n")
+        f.write("# %-48s %5s %5s %5s %6s %6s %8s %8s %8s\n" % ("kernel", "WGs", "gridY", "VGPR", "LDS", "calls", "avg_us",
+                                                            "med_us", "min_us"))
+        for key in sorted(rows):
+            v = rows[key]
+            f.write("  %-48s %5d %5d %5s %6s %6d %8.2f %8.2f %8.2f\n" % (key[0][:48], key[1], key[2], key[3], key[4], len(v),
+                                                                      sum(v) / len(v), statistics.median(v), min(v)))
+        f.write("\n# kernel stats (library rows)\n")
+        with open(stats_csv) as g:
+            lines = g.read().splitlines()
+        f.write(lines[0] + "\n")
+        for line in lines[1:]:
+            if "bl::" in line:
+                f.write(line + "\n")
+    log("wrote %s" % out)
+
+
 def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
     import csv
 
@@ -254,9 +294,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "STATS_CSV", "OUT"))
     ap.add_argument("--copy-bytes", type=int, default=256 << 20)
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_bytes, TRAFFIC_FILE)
         return 0
