@@ -155,8 +155,10 @@ __device__ __forceinline__ void row_load(const float* __restrict__ u, int K, con
     }
 }
 
-// Statistics from values preloaded by row_load (KEEP > 0) or read here.
-template <int KEEP>
+// Statistics from values preloaded by row_load (KEEP > 0) or read here. WIDE keeps eight
+// loads per thread in flight over the groups it reads itself (for long rows in the
+// standalone quantizer; the summation order is unchanged, only registers grow).
+template <int KEEP, bool WIDE = false>
 __device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const float* __restrict__ gain, int act,
                                   bool want_sumsq, const float* __restrict__ up,
                                   const float4 (&xa)[KEEP > 0 ? KEEP : 1], const float4 (&gb)[KEEP > 0 ? KEEP : 1],
@@ -200,6 +202,24 @@ __device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const floa
         }
         g += KEEP * 256;
     }
+    // groups past the kept ones (WIDE: eight loads in flight per thread, visited in order,
+    // which is the same summation order as one group at a time)
+    for (; WIDE && g + 7 * 256 < G; g += 8 * 256) {
+        float4 a[8], gv[8], uv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            a[q] = reinterpret_cast<const float4*>(u)[g + q * 256];
+            gv[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            uv[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            if (gain)
+                gv[q] = reinterpret_cast<const float4*>(gain)[g + q * 256];
+            if (up)
+                uv[q] = reinterpret_cast<const float4*>(up)[g + q * 256];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            visit(a[q], gv[q], uv[q]);
+    }
     for (; g < G; g += 256) {
         const float4 a = reinterpret_cast<const float4*>(u)[g];
         float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
@@ -228,14 +248,14 @@ __device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const floa
     return RowStats{m, total};
 }
 
-template <int KEEP = 0>
+template <int KEEP = 0, bool WIDE = false>
 __device__ RowStats row_stats(const float* __restrict__ u, int K, const float* __restrict__ gain, int act,
                               bool want_sumsq, const float* __restrict__ up, int slot, float4* wk = nullptr)
 {
     float4 xa[KEEP > 0 ? KEEP : 1], gb[KEEP > 0 ? KEEP : 1];
     if constexpr (KEEP > 0)
         row_load<KEEP>(u, K, gain, up, xa, gb);
-    return row_stats_pre<KEEP>(u, K, gain, act, want_sumsq, up, xa, gb, wk, slot);
+    return row_stats_pre<KEEP, WIDE>(u, K, gain, act, want_sumsq, up, xa, gb, wk, slot);
 }
 
 __device__ __forceinline__ void token_scales(const RowStats& st, int K, bool norm, float eps, float& sp, float& s)

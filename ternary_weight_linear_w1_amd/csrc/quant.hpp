@@ -33,13 +33,14 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(QuantArgs a)
         const float* u = a.X + t * stride;
         const float* up = a.act == 2 ? u + a.K : nullptr;
         const bool norm = a.gain != nullptr;
-        const RowStats st = row_stats(u, a.K, a.gain, a.act, norm, up, calls++ & 1);
+        const RowStats st = row_stats<0, true>(u, a.K, a.gain, a.act, norm, up, calls++ & 1);
         float sp, s;
         token_scales(st, a.K, norm, a.eps, sp, s);
         if (threadIdx.x == 0)
             a.scale[t] = s;
         uint32_t* out = reinterpret_cast<uint32_t*>(a.Xq + t * (int64_t)a.K);
         const int G = a.K >> 2;
+#pragma unroll 4
         for (int g = threadIdx.x; g < G; g += 256) {
             const float4 x = reinterpret_cast<const float4*>(u)[g];
             float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
