@@ -195,17 +195,44 @@ void launch_gemm(const bl::FwdArgs& f, hipStream_t stream)
                        stream, a);
 }
 
+// Resident blocks per CU of a kernel on the current device (queried once per device).
+template <typename Kern>
+int resident_blocks(Kern kernel, std::atomic<int> (&cache)[kMaxDevices])
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 1;
+    int occ = cache[dev].load(std::memory_order_relaxed);
+    if (occ <= 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0) != hipSuccess || occ <= 0)
+            occ = 1;
+        cache[dev].store(occ, std::memory_order_relaxed);
+    }
+    return occ;
+}
+
+std::atomic<int> g_occ_gemm_big[kMaxDevices];
+
 bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
 {
     if (a.M < 16 || a.M > INT32_MAX || (a.K % 64) != 0)
         return false;
     if (((a.M + 31) / 32) * ((a.N + 127) / 128) >= INT32_MAX)
         return false;
-    // Tile shapes from timing the 2B prefill (M = 512, 2048) and 100B (M = 64) shapes.
-    if (a.M >= 1024)
-        launch_gemm<64, 256, 1, 4, 2, 128>(a, stream);
-    else
-        launch_gemm<32, 128, 1, 4, 2, 256>(a, stream);
+    // Tile shapes from timing the 2B prefill (M = 512, 2048) and 100B (M = 64) shapes: the
+    // 64 x 256 tile (K steps of 128) is faster per tile, but a launch that leaves most of
+    // its last round of resident blocks empty loses to 32 x 128 tiles (K steps of 256).
+    if (a.M >= 1024) {
+        const int64_t tiles = ((a.M + 63) / 64) * ((a.N + 255) / 256);
+        const int64_t slots = int64_t(cu_count()) *
+                              resident_blocks(bl::gemm_mfma_kernel<64, 256, 1, 4, 2, false, 128>, g_occ_gemm_big);
+        const int64_t rounds = (tiles + slots - 1) / slots;
+        if (2 * tiles >= rounds * slots) {
+            launch_gemm<64, 256, 1, 4, 2, 128>(a, stream);
+            return true;
+        }
+    }
+    launch_gemm<32, 128, 1, 4, 2, 256>(a, stream);
     return true;
 }
 
