@@ -186,12 +186,12 @@ void launch_generic(const bl::FwdArgs& a, hipStream_t stream)
 }
 
 // Many tokens: int8 MFMA GEMM. Needs K % 64 == 0 and 16-byte aligned operands.
-template <int BM, int BN, int WM, int WN, int P, int BK>
+template <int BM, int BN, int WM, int WN, int P, int BK, int WK = 1>
 void launch_gemm(const bl::FwdArgs& f, hipStream_t stream)
 {
     bl::GemmArgs a{f.Xq, f.xscale, f.W, f.gamma, f.Y, f.acc, (int)f.M, (int)f.N, f.K, f.residual};
     const int64_t tiles = ((f.M + BM - 1) / BM) * ((f.N + BN - 1) / BN);
-    hipLaunchKernelGGL((bl::gemm_mfma_kernel<BM, BN, WM, WN, P, false, BK>), dim3((unsigned)tiles), dim3(256), 0,
+    hipLaunchKernelGGL((bl::gemm_mfma_kernel<BM, BN, WM, WN, P, false, BK, WK>), dim3((unsigned)tiles), dim3(256), 0,
                        stream, a);
 }
 
@@ -212,6 +212,7 @@ int resident_blocks(Kern kernel, std::atomic<int> (&cache)[kMaxDevices])
 }
 
 std::atomic<int> g_occ_gemm_big[kMaxDevices];
+std::atomic<int> g_occ_gemm_small[kMaxDevices];
 
 bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
 {
@@ -232,7 +233,15 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
             return true;
         }
     }
-    launch_gemm<32, 128, 1, 4, 2, 256>(a, stream);
+    // Few tokens and few output tiles (long rows at M = 64): 32 x 64 tiles whose four waves
+    // split N in two and K in two, so twice as many blocks cover the GPU.
+    const int64_t tiles = ((a.M + 31) / 32) * ((a.N + 127) / 128);
+    const int64_t slots = int64_t(cu_count()) *
+                          resident_blocks(bl::gemm_mfma_kernel<32, 128, 1, 4, 2, false, 256>, g_occ_gemm_small);
+    if (4 * tiles <= slots)
+        launch_gemm<32, 64, 1, 2, 2, 256, 2>(a, stream);
+    else
+        launch_gemm<32, 128, 1, 4, 2, 256>(a, stream);
     return true;
 }
 

@@ -59,18 +59,23 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-template <int BM, int BN, int WM, int WN, int P, bool SCHED = false, int BK = 128>
+// WK > 1 splits K inside the block: each step stages WK * BK columns of activations and
+// wave group g (of WM x WN waves) multiplies columns g*BK .. g*BK + BK - 1; the groups'
+// int32 partial sums are added through LDS before the epilogue (exact, fixed order).
+// This gives narrow tiles (and so more blocks) for few tokens and long rows.
+template <int BM, int BN, int WM, int WN, int P, bool SCHED = false, int BK = 128, int WK = 1>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
 {
-    static_assert(WM * WN == 4, "four waves per block");
+    static_assert(WM * WN * WK == 4, "four waves per block");
     constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
     constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
     static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(BK == 128 || BK == 256, "K step of 128 or 256");
-    constexpr int KS = BK / 32;                  // MFMA k-substeps per step
+    constexpr int KS = BK / 32;                  // MFMA k-substeps per step (per wave group)
     constexpr int BH = BK / 128;                 // 16-byte weight loads per fragment per step
-    constexpr int AST = BK + 16;                 // LDS row stride in bytes (padded)
-    constexpr int UPR = BK / 16;                 // 16-byte activation units per row
+    constexpr int SK = BK * WK;                  // columns staged per step
+    constexpr int AST = SK + 16;                 // LDS row stride in bytes (padded)
+    constexpr int UPR = SK / 16;                 // 16-byte activation units per row
     constexpr int AU = BM * UPR / 256;           // 16-byte activation units per thread per step
     static_assert(AU >= 1, "block tile too small");
 
@@ -81,7 +86,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int wk = wave / (WM * WN);
+    const int wm = (wave % (WM * WN)) / WN, wn = wave % WN;
     const int M = a.M, N = a.N, K = a.K;
     const int KB = K >> 2;
 
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
         aoff[i] = ((tid + 256 * i) / UPR) * K + 16 * (tid % UPR);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
-        boff[fn] = (wn * TN + fn * 32 + (lane & 31)) * KB + 16 * (lane >> 5);
+        boff[fn] = (wn * TN + fn * 32 + (lane & 31)) * KB + 16 * (lane >> 5) + (wk * BK) / 4;
     const int acol = 16 * (tid % UPR);        // k offset of this thread's activation unit
 
     // Prefetch ring: the loads for step it + P are issued while step it is computed.
@@ -161,11 +167,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
             for (int r = 0; r < 16; ++r)
                 C[fm][fn][r] = 0;
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (K + SK - 1) / SK;
 #pragma unroll
     for (int s = 0; s < P; ++s)
         if (s < nk)
-            load(areg[s], breg[s], s * BK);
+            load(areg[s], breg[s], s * SK);
     store_a(areg[0], 0, K);
     __syncthreads();
 
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
             const int it = it0 + s;
             if (it < nk) {
                 const int buf = it & 1;
-                const int kvalid = K - it * BK;   // valid k within this step
+                const int kvalid = K - it * SK - wk * BK;   // valid k within this group's columns
                 u32x4 bcur[FN][BH];
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
                             bcur[fn][h] = u32x4{0u, 0u, 0u, 0u};
                     }
                 if (it + P < nk)
-                    load(areg[s], breg[s], (it + P) * BK);
+                    load(areg[s], breg[s], (it + P) * SK);
                 // All operands of the step first (one LDS round trip, unpack on the
                 // VALU), then the 4 * FM * FN matrix instructions back to back.
                 const uint8_t* Ab = As[buf];
@@ -196,8 +202,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
 #pragma unroll
                     for (int fm = 0; fm < FM; ++fm) {
                         const int r = wm * TM + fm * 32 + (lane & 31);
-                        af[ks][fm] = *reinterpret_cast<const v4i*>(Ab + r * AST + 128 * (ks >> 2) + 64 * (lane >> 5) +
-                                                                   16 * (ks & 3));
+                        af[ks][fm] = *reinterpret_cast<const v4i*>(Ab + r * AST + wk * BK + 128 * (ks >> 2) +
+                                                                   64 * (lane >> 5) + 16 * (ks & 3));
                     }
                 v4i bf[KS][FN];
 #pragma unroll
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
                     }
                 }
                 if (it + 1 < nk)
-                    store_a(areg[(s + 1) % P], buf ^ 1, K - (it + 1) * BK);
+                    store_a(areg[(s + 1) % P], buf ^ 1, K - (it + 1) * SK);
                 __syncthreads();
             }
         }
@@ -246,6 +252,36 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
             rsum[(tid + 256 * i) / UPR] = v;
     }
     __syncthreads();
+
+    if constexpr (WK > 1) {
+        // partial sums of wave groups 1.. through LDS into group 0 (the staging buffers are
+        // free: every wave has passed the last step's barrier)
+        static_assert((WK - 1) * WM * WN * FM * FN * 16 * 64 * 4 <= 2 * BM * AST, "reduction fits in LDS");
+        int32_t* red = reinterpret_cast<int32_t*>(&As[0][0]);
+        const int slot_base = ((wm * WN + wn) * FM * FN) * 16 * 64;
+        if (wk > 0) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        red[(wk - 1) * WM * WN * FM * FN * 16 * 64 + slot_base + ((fm * FN + fn) * 16 + r) * 64 + lane] =
+                            C[fm][fn][r];
+        }
+        __syncthreads();
+        if (wk > 0)
+            return;
+#pragma unroll
+        for (int g = 1; g < WK; ++g)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        C[fm][fn][r] += red[(g - 1) * WM * WN * FM * FN * 16 * 64 + slot_base + ((fm * FN + fn) * 16 + r) * 64 + lane];
+    }
 
     // C layout of a 32x32 tile: lane l, register r -> column l % 32,
     // row 8 (r / 4) + 4 (l / 32) + r % 4. Each row's offset and scale are read once.
