@@ -65,12 +65,12 @@ constexpr int keep_groups()
 // Early loads of token 0 of a tile: the fp32 row (fused) or the int8 codes, issued
 // before the weight loads so that they are not queued behind them.
 constexpr int kPreUnits = 2;  // 16-byte int8 units per thread preloaded (K <= 8192)
-template <int KP>
+template <int KP, int MT>
 struct Pre {
     float4 xa[KP];
     float4 gb[KP];         // gain, or the up values when gated
     uint4 q[kPreUnits];
-    float xs[4];           // per-token scales of the tile (unfused)
+    float xs[MT];          // per-token scales of the tile (unfused)
 };
 
 __device__ __forceinline__ int64_t x_stride(const FwdArgs& a)
@@ -78,8 +78,8 @@ __device__ __forceinline__ int64_t x_stride(const FwdArgs& a)
     return a.act == 2 ? 2 * (int64_t)a.K : (int64_t)a.K;
 }
 
-template <bool FUSED, bool STAGE, int KP>
-__device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre<KP>& p)
+template <bool FUSED, bool STAGE, int KP, int MT>
+__device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre<KP, MT>& p)
 {
     if constexpr (FUSED) {
         const float* x = a.X + tok * x_stride(a);
@@ -98,16 +98,16 @@ __device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre
         // wait sits in front of the weight loads
         const int64_t left = a.M - tok;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(a.xscale + tok), (short)0, (int)(4 * (left < 4 ? left : 4)), kBufFlags);
+            (void*)(a.xscale + tok), (short)0, (int)(4 * (left < MT ? left : MT)), kBufFlags);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < MT; ++t)
             p.xs[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * t, 0, 0));
     }
 }
 
 template <int MT, bool FUSED, int KP>
 __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt, uint4* __restrict__ lds,
-                                            float (&s)[MT], const Pre<KP>& pre)
+                                            float (&s)[MT], const Pre<KP, MT>& pre)
 {
     constexpr int NT = 256;
     const int tid = threadIdx.x;
@@ -163,7 +163,7 @@ __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt
                 words[g] = group_codes(make_float4(wa[0], wa[1], wa[2], wa[3]), sp);
             }
         } else {
-            s[t] = pre.xs[t < 4 ? t : 0];
+            s[t] = pre.xs[t];
             const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
             int u = tid;
             if (t == 0) {
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
         // Activations of token 0 first, then the first two passes of weights, then the
         // prologue arithmetic while the weights are in flight.
         constexpr bool DIRECT = !FUSED && L >= 64;
-        Pre<keep_groups<L, CPL>()> pre;
+        Pre<keep_groups<L, CPL>(), MT> pre;
         stage_preload<FUSED, !DIRECT>(a, t0, pre);
         uint32_t act[MT][CPL][16];
         if constexpr (DIRECT) {
@@ -359,13 +359,15 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
             int32_t accv[R][MT];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                // four independent accumulators (one per dword of a chunk) keep the dot4
-                // chain short; integer addition makes the split exact
-                int32_t part[MT][4];
+                // independent accumulators (one per dword of a chunk for one or two tokens;
+                // with more tokens the tokens themselves are independent chains) keep the
+                // dot4 chains short; integer addition makes the split exact
+                constexpr int NP = MT >= 4 ? 1 : 4;
+                int32_t part[MT][NP];
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
 #pragma unroll
-                    for (int d = 0; d < 4; ++d)
+                    for (int d = 0; d < NP; ++d)
                         part[t][d] = 0;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
@@ -377,13 +379,19 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
                             const uint32_t u = (wd[d] >> (2 * f)) & 0x03030303u;
 #pragma unroll
                             for (int t = 0; t < MT; ++t)
-                                part[t][d] = __builtin_amdgcn_sdot4((int)u, (int)act[t][i][4 * d + f], part[t][d], false);
+                                part[t][d % NP] =
+                                    __builtin_amdgcn_sdot4((int)u, (int)act[t][i][4 * d + f], part[t][d % NP], false);
                         }
                     }
                 }
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    accv[r][t] = group_sum<(L < 64 ? L : 64)>(((part[t][0] + part[t][1]) + (part[t][2] + part[t][3])) - xs[t]);
+                {
+                    int32_t sum = part[t][0];
+                    if constexpr (NP == 4)
+                        sum = (part[t][0] + part[t][1]) + (part[t][2] + part[t][3]);
+                    accv[r][t] = group_sum<(L < 64 ? L : 64)>(sum - xs[t]);
+                }
             }
             if constexpr (L > 64) {
                 if ((tid & 63) == 0) {
