@@ -121,7 +121,19 @@ bool dispatch_mt1(const bl::FwdArgs& a, hipStream_t stream)
 {
     const int KC = a.K / 64;
     const bool big = a.N * (int64_t)a.K >= (int64_t(64) << 20);   // >= 16 MB of packed weights
-    if (KC <= 48) { launch_k64<16, 1, 3, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 48) {
+        // fused, 2B-sized rows: shorter matrices take 32 lanes x 2 chunks (more blocks),
+        // longer ones two rows per lane (graph-timed on the 2B layer)
+        if constexpr (FUSED) {
+            if (a.N <= 4096)
+                launch_k64<32, 1, 2, 1, FUSED>(a, 1, stream);
+            else
+                launch_k64<16, 1, 3, 2, FUSED>(a, 1, stream);
+        } else {
+            launch_k64<16, 1, 3, 1, FUSED>(a, 2, stream);
+        }
+        return true;
+    }
     if (KC <= 64) { launch_k64<16, 1, 4, 1, FUSED>(a, 2, stream); return true; }
     if (KC <= 128) {
         if (!big)
