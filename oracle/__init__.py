@@ -4,8 +4,10 @@
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
 leg of ``bench.py`` import this package. The product library never uses it.
 
-Every function takes and returns numpy arrays; the arithmetic is in the C file,
-whose header lists the passages each step follows.
+Every function takes and returns numpy arrays. The BitLinear arithmetic is in the C
+file, whose header lists the passages each step follows; the decode attention (rotary
+positions, bf16 key/value cache, softmax attention) is plain numpy at the end of this
+file, each function citing its passage.
 """
 from __future__ import annotations
 
@@ -226,12 +228,16 @@ def attention_ctx1(qkv: np.ndarray, heads: int, kv_heads: int, head_dim: int) ->
     return out.reshape(m, heads * head_dim)
 
 
-def decode_layer(h: np.ndarray, mats: dict, gains: dict, dims: dict, gated: bool, eps: float = 1e-5):
+def decode_layer(h: np.ndarray, mats: dict, gains: dict, dims: dict, gated: bool, eps: float = 1e-5,
+                 cache=None):
     """One BitNet decode layer on fp32 h [M][H] (standard Transformer block with BitLinear
     in place of nn.Linear: BitNet b1.58 深度解析 s.2.4; subln before O and down and ReLU^2:
     微软AI大模型炸场 s.1-2). mats[name] = (codes int8 [N][K], gamma) for qkv, o, up
     ([2F][K] gate rows then up rows when gated), down; gains g_in, g_attn, g_post, g_ffn.
-    Residual adds are fp32. Returns the new h and the intermediates."""
+    Residual adds are fp32. Attention runs at context length 1 (attention_ctx1) unless
+    cache = dict(k, v, pos, theta) is given: then attention_decode over that cache, whose
+    updated arrays are returned among the intermediates as k and v.
+    Returns the new h and the intermediates."""
     def lin(x, name, gain, act):
         q, gamma = mats[name]
         xq, s = quantize_act_norm(x, gain, eps, act)
@@ -239,8 +245,112 @@ def decode_layer(h: np.ndarray, mats: dict, gains: dict, dims: dict, gated: bool
 
     f32 = np.float32
     qkv = lin(h, "qkv", gains["g_in"], 0)
-    o = attention_ctx1(qkv, dims["heads"], dims["kv_heads"], dims["head_dim"])
+    extra = {}
+    if cache is None:
+        o = attention_ctx1(qkv, dims["heads"], dims["kv_heads"], dims["head_dim"])
+    else:
+        o, extra["k"], extra["v"] = attention_decode(qkv, cache["k"], cache["v"], cache["pos"], dims["heads"],
+                                                     dims["kv_heads"], cache["theta"])
+        o = o.astype(f32)
     h1 = (h.astype(f32) + lin(o, "o", gains["g_attn"], 0)).astype(f32)
     u = lin(h1, "up", gains["g_post"], 0)
     h2 = (h1 + lin(u, "down", gains["g_ffn"], 2 if gated else 1)).astype(f32)
-    return h2, dict(qkv=qkv, o=o, h1=h1, u=u)
+    return h2, dict(qkv=qkv, o=o, h1=h1, u=u, **extra)
+
+
+# --------------------------------------------------------------------------------------
+# Decode attention at real context length: rotary positions, a bf16 key/value cache and
+# grouped-query softmax attention. Plain numpy, binary64 unless a step states otherwise.
+# --------------------------------------------------------------------------------------
+
+def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
+    """Rotation frequency of pair i: theta^(-2i/D), i = 0 .. D/2-1, in binary64 (rotary
+    position embedding, 微软AI大模型炸场 s.2 "特殊设计"; the pages name the method only:
+    the original rotary frequencies and base are taken)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(np.float64(theta), -(2.0 * i) / head_dim)
+
+
+def rope(x: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    """Rotary embedding of head vectors x [..., D] at position pos, binary64: dimension i
+    and dimension i + D/2 form a plane rotated by the angle pos * theta^(-2i/D)."""
+    x = np.asarray(x, dtype=np.float64)
+    h = x.shape[-1] // 2
+    a = pos * rope_inv_freq(2 * h, theta)
+    c, s = np.cos(a), np.sin(a)
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def rope_f32(x: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    """The same rotation evaluated in binary32, for keys whose rotated value is rounded
+    into the bf16 cache (a rounding decision taken in the kernel's precision): cos and
+    sin of the binary64 angle rounded once to binary32, then x1*c - x2*s and x2*c + x1*s
+    with every product and the sum rounded to binary32 (no fused multiply-add)."""
+    x = np.asarray(x, dtype=np.float32)
+    h = x.shape[-1] // 2
+    a = pos * rope_inv_freq(2 * h, theta)
+    c, s = np.cos(a).astype(np.float32), np.sin(a).astype(np.float32)
+    x1, x2 = x[..., :h], x[..., h:]
+    lo = np.subtract(np.multiply(x1, c, dtype=np.float32), np.multiply(x2, s, dtype=np.float32), dtype=np.float32)
+    hi = np.add(np.multiply(x2, c, dtype=np.float32), np.multiply(x1, s, dtype=np.float32), dtype=np.float32)
+    return np.concatenate([lo, hi], axis=-1)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Finite binary32 values to bfloat16 bit patterns (uint16), rounding to nearest with
+    ties to even: bfloat16 keeps 8 significant bits and binary32's exponent range, so a
+    value m * 2^e (0.5 <= |m| < 1) is rounded to a multiple of 2^(e-8), never finer than
+    the smallest bfloat16 step 2^-133."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    _, e = np.frexp(x)
+    quantum = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(x / quantum) * quantum           # x / quantum is exact; rint is half-even
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """Value of bfloat16 bit patterns, as binary64 (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def attention_decode(qkv: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos, heads: int,
+                     kv_heads: int, theta: float):
+    """One decode step of scaled dot-product attention (BitNet b1.58 深度解析 s.2.4 block
+    diagram) with rotary positions (微软AI大模型炸场 s.2) over a key/value cache.
+
+    qkv [M][(heads + 2 kv_heads) D] fp32 holds the new token's query heads, then key heads,
+    then value heads. k_cache / v_cache are bf16 bit patterns [M][kv_heads][C][D]; pos [M]
+    is the new token's position. For each sequence b with 0 <= pos[b] < C:
+      1. the new key is rotated at pos (rope_f32) and it and the new value are rounded
+         to bf16 into slot pos of the caches;
+      2. query head h (of group h // (heads / kv_heads)) is rotated at pos in binary64
+         and scores s_j = q . k_j / sqrt(D) over cached positions j = 0 .. pos;
+      3. out_h = sum_j softmax(s)_j v_j.
+    A sequence with pos outside [0, C) gets NaN outputs and leaves its caches untouched.
+    Returns (out float64 [M][heads D], new k_cache, new v_cache)."""
+    qkv = np.asarray(qkv, dtype=np.float32)
+    m = qkv.shape[0]
+    _, _, cap, d = k_cache.shape
+    kc, vc = k_cache.copy(), v_cache.copy()
+    group = heads // kv_heads
+    out = np.full((m, heads, d), np.nan)
+    for b in range(m):
+        p = int(pos[b])
+        if not 0 <= p < cap:
+            continue
+        q = qkv[b, :heads * d].reshape(heads, d)
+        k = qkv[b, heads * d:(heads + kv_heads) * d].reshape(kv_heads, d)
+        v = qkv[b, (heads + kv_heads) * d:(heads + 2 * kv_heads) * d].reshape(kv_heads, d)
+        kc[b, :, p, :] = round_bf16(rope_f32(k, p, theta))
+        vc[b, :, p, :] = round_bf16(v)
+        qr = rope(q, p, theta)
+        for h in range(heads):
+            g = h // group
+            keys = bf16_value(kc[b, g, :p + 1])
+            vals = bf16_value(vc[b, g, :p + 1])
+            s = keys @ qr[h] / np.sqrt(d)
+            w = np.exp(s - s.max())
+            out[b, h] = (w / w.sum()) @ vals
+    return out.reshape(m, heads * d), kc, vc

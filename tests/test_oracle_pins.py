@@ -476,3 +476,148 @@ def test_unpack5_flags_invalid_bytes_and_padding(ora):
     packed[0, 2] = 0                      # covers codes 10..14: 12..14 lie past K = 12
     _, bad = ora.unpack5(packed, 12)
     assert bad == 1 + 3
+
+
+# ----------------------------------------------------------------------------- attention at real context
+
+def test_rope_golden(ora, golden):
+    """Hand example at D = 4: catches a swapped pairing ((2i, 2i+1) instead of (i, i+D/2)),
+    a wrong frequency exponent or a sign flip in the rotation."""
+    g = golden["rope_hand"]
+    x = np.array(g["x"])
+    got = ora.rope(x, g["pos"], g["theta"])
+    assert np.allclose(got, g["expect"], rtol=0, atol=1e-15)
+    got32 = ora.rope_f32(x, g["pos"], g["theta"])
+    assert np.allclose(got32, g["expect"], rtol=2 ** -22, atol=0)
+
+
+def test_rope_position_zero_and_norms(ora):
+    """Position 0 rotates by 0 (identity, also in binary32); every pair keeps its length."""
+    x = datagen.outlier_acts(5, 128, 801)
+    assert (ora.rope(x, 0, 10000.0) == x.astype(np.float64)).all()
+    assert (ora.rope_f32(x, 0, 10000.0) == x).all()
+    y = ora.rope(x, 4095, 10000.0)
+    n0 = np.hypot(x[:, :64].astype(np.float64), x[:, 64:].astype(np.float64))
+    n1 = np.hypot(y[:, :64], y[:, 64:])
+    assert np.allclose(n0, n1, rtol=1e-13, atol=0)
+
+
+def test_rope_scores_depend_on_relative_position_only(ora):
+    """The defining property of rotary embedding: <R(a) q, R(b) k> = <R(a+t) q, R(b+t) k>.
+    Catches per-dimension (not per-pair) angles or a frequency that varies with position."""
+    q = datagen.outlier_acts(3, 128, 802).astype(np.float64)
+    k = datagen.outlier_acts(3, 128, 803).astype(np.float64)
+    for a, b, t in ((7, 3, 100), (0, 4000, 95), (1234, 1234, 2000)):
+        s0 = np.sum(ora.rope(q, a, 10000.0) * ora.rope(k, b, 10000.0), axis=1)
+        s1 = np.sum(ora.rope(q, a + t, 10000.0) * ora.rope(k, b + t, 10000.0), axis=1)
+        scale = np.sum(np.abs(q) * np.abs(k), axis=1)
+        assert (np.abs(s0 - s1) <= 1e-10 * scale).all()
+
+
+def test_rope_f32_within_binary32_bound_of_rope(ora):
+    """The binary32 evaluation differs from the binary64 rotation by at most the rounding
+    of c, s, two products and a sum: 3 * 2^-24 * (|x1| + |x2|) per output."""
+    x = datagen.outlier_acts(16, 128, 804)
+    for pos in (1, 17, 4095, 131071):
+        y64 = ora.rope(x, pos, 10000.0)
+        y32 = ora.rope_f32(x, pos, 10000.0).astype(np.float64)
+        mag = np.abs(x[:, :64]).astype(np.float64) + np.abs(x[:, 64:])
+        bound = 3 * 2.0 ** -24 * np.concatenate([mag, mag], axis=1)
+        assert (np.abs(y64 - y32) <= bound).all(), pos
+
+
+def test_round_bf16_golden_and_torch(ora, golden):
+    """Hand cases (ties to even, just above a tie, subnormal) and torch's float32 to
+    bfloat16 conversion (round to nearest even) on random values, exact ties included."""
+    import torch
+    g = golden["bf16_round"]
+    assert ora.round_bf16(np.array(g["x"], np.float32)).tolist() == g["bits"]
+    rng = datagen.rng(805)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
+    ties = (x.view(np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    x = np.concatenate([x, ties.view(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (ora.round_bf16(x) == ref).all()
+    assert (ora.bf16_value(ref) == torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy()).all()
+
+
+def _one_seq(q, k, v, heads, kv_heads, d):
+    return np.concatenate([np.ravel(q), np.ravel(k), np.ravel(v)]).astype(np.float32)[None, :]
+
+
+def test_attention_golden(ora, golden):
+    """Two positions with hand-computed softmax weights: catches a missing 1/sqrt(D), a
+    query left unrotated, or the new key/value not entering the softmax."""
+    g = golden["attention_hand"]
+    qkv = _one_seq(g["q"], g["k_new"], g["v_new"], 1, 1, 2)
+    kc = np.zeros((1, 1, 4, 2), np.uint16)
+    vc = np.zeros((1, 1, 4, 2), np.uint16)
+    kc[0, 0, 0] = ora.round_bf16(np.array(g["k0"], np.float32))
+    vc[0, 0, 0] = ora.round_bf16(np.array(g["v0"], np.float32))
+    out, kc2, vc2 = ora.attention_decode(qkv, kc, vc, [g["pos"]], 1, 1, g["theta"])
+    assert np.allclose(out[0], g["expect"], rtol=1e-14, atol=0)
+    assert (ora.bf16_value(vc2[0, 0, 1]) == np.array(g["v_new"])).all()
+    assert (kc2[0, 0, 1] == 0).all() and (kc2[0, 0, 2:] == 0).all()
+
+
+def test_attention_first_position_copies_value_per_group(ora):
+    """At position 0 the softmax has one term, so query head h returns its group's new
+    value (bf16-rounded): with 4 query heads on 2 KV heads the output is v0, v0, v1, v1.
+    Catches a wrong head-to-group map (h % kv_heads instead of h // group)."""
+    d = 8
+    q = datagen.outlier_acts(4, d, 806)
+    k = datagen.outlier_acts(2, d, 807)
+    v = datagen.outlier_acts(2, d, 808)
+    kc = np.zeros((1, 2, 3, d), np.uint16)
+    out, _, vc = ora.attention_decode(_one_seq(q, k, v, 4, 2, d), kc, kc.copy(), [0], 4, 2, 10000.0)
+    v16 = ora.bf16_value(ora.round_bf16(v))
+    assert (out[0].reshape(4, d) == v16[[0, 0, 1, 1]]).all()
+    assert (vc[0, :, 0] == ora.round_bf16(v)).all()
+
+
+def test_attention_equal_keys_average_values(ora):
+    """Every cached key equal to the new rotated key: all scores tie and the output is
+    the plain mean of the value rows 0..pos (numpy mean)."""
+    d, pos, cap = 16, 37, 50
+    rng = datagen.rng(809)
+    q = rng.standard_normal((2, d)).astype(np.float32)
+    k = rng.standard_normal((1, d)).astype(np.float32)
+    v = rng.standard_normal((1, d)).astype(np.float32)
+    krot = ora.round_bf16(ora.rope_f32(k, pos, 10000.0))
+    kc = np.broadcast_to(krot, (1, 1, cap, d)).copy()
+    vc = ora.round_bf16(rng.standard_normal((1, 1, cap, d)).astype(np.float32))
+    out, _, vc2 = ora.attention_decode(_one_seq(q, k, v, 2, 1, d), kc, vc, [pos], 2, 1, 10000.0)
+    mean = ora.bf16_value(vc2[0, 0, :pos + 1]).mean(axis=0)
+    assert np.allclose(out[0].reshape(2, d), mean[None, :], rtol=1e-13, atol=1e-15)
+
+
+def test_attention_dominant_key_and_extent(ora):
+    """A cached key along the rotated query with score about 77 (the others stay near 0,
+    so their weights are below e^-70) returns its value; slots after pos hold NaN here
+    and must never be read."""
+    d, pos, cap, hot = 32, 20, 30, 9
+    rng = datagen.rng(810)
+    q = rng.standard_normal((1, d)).astype(np.float32)
+    k = rng.standard_normal((1, d)).astype(np.float32)
+    v = rng.standard_normal((1, d)).astype(np.float32)
+    kc = ora.round_bf16(0.1 * rng.standard_normal((1, 1, cap, d)).astype(np.float32))
+    vc = ora.round_bf16(rng.standard_normal((1, 1, cap, d)).astype(np.float32))
+    qr = ora.rope(q, pos, 10000.0)[0]
+    kc[0, 0, hot] = ora.round_bf16((60.0 * qr / np.linalg.norm(qr)).astype(np.float32))
+    nan16 = np.uint16(0x7FC0)
+    kc[0, 0, pos + 1:] = nan16
+    vc[0, 0, pos + 1:] = nan16
+    out, kc2, vc2 = ora.attention_decode(_one_seq(q, k, v, 1, 1, d), kc, vc, [pos], 1, 1, 10000.0)
+    assert np.allclose(out[0], ora.bf16_value(vc[0, 0, hot]), rtol=0, atol=1e-28)
+    assert (kc2[0, 0, pos + 1:] == nan16).all() and (vc2[0, 0, :pos] == vc[0, 0, :pos]).all()
+
+
+def test_attention_invalid_position(ora):
+    """A position outside [0, C) gives NaN outputs and leaves both caches as they were."""
+    d = 8
+    qkv = datagen.outlier_acts(2, 3 * d, 811)
+    kc = ora.round_bf16(datagen.outlier_acts(2 * 4, d, 812)).reshape(2, 1, 4, d)
+    vc = kc.copy()
+    out, kc2, vc2 = ora.attention_decode(qkv, kc, vc, [4, -1], 1, 1, 10000.0)
+    assert np.isnan(out).all()
+    assert (kc2 == kc).all() and (vc2 == vc).all()
