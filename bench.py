@@ -499,10 +499,16 @@ def run_extra(torch, bl, datagen, dev, mats2b):
     # ---- five codes per byte (1.6 bits per weight) against the 2-bit fields, pre-quantized
     res["trits5_vs_2bit"] = run_trits5(torch, bl, datagen, dev)
     torch.cuda.empty_cache()
-    # ---- decode stack: 30 layers of the 2B shapes at M = 1, plain and gated FFN
+    # ---- decode attention over a bf16 key/value cache at real context length
+    res["attention_decode"] = run_attention(torch, bl, dev)
+    torch.cuda.empty_cache()
+    # ---- decode stack: 30 layers of the 2B shapes at M = 1, plain and gated FFN, attending
+    #      over 1 and over 4096 cached positions
     for gated in (False, True):
-        res["2B_stack30_M1" + ("_gated" if gated else "")] = run_stack(torch, bl, datagen, dev, gated)
-        torch.cuda.empty_cache()
+        for ctx in (1, 4096):
+            key = "2B_stack30_M1_ctx%d" % ctx + ("_gated" if gated else "")
+            res[key] = run_stack(torch, bl, datagen, dev, gated, ctx=ctx)
+            torch.cuda.empty_cache()
     # ---- packing rate (100B up projection)
     N, K = 28672, 8192
     w = datagen.gg_weights_torch(N, K, datagen.stream_id(5, 9, 0, 0), dev)
@@ -548,10 +554,49 @@ def run_trits5(torch, bl, datagen, dev):
 STACK_DIMS = dict(hidden=2560, heads=20, kv_heads=5, head_dim=128, ffn=6912)
 
 
-def run_stack(torch, bl, datagen, dev, gated, n_layers=30, copies=2, replays=20):
-    """Per-token latency of a 30-layer decode stack (one launch per BitLinear plus the
-    attention copy), as a HIP graph over `copies` weight copies of the stack so that each
-    pass streams its weights from HBM (>= 776 MB against 256 MB of MALL)."""
+def attention_bytes(M, heads, kv_heads, ctx, d=128):
+    """Algorithmic HBM bytes of one decode-attention call with every sequence at position
+    ctx - 1: cached keys and values read (ctx - 1 rows each, bf16), the new key and value
+    appended, the qkv vector read and the output written (fp32)."""
+    return M * (2 * kv_heads * (ctx - 1) * d * 2 + 2 * kv_heads * d * 2 + (heads + 2 * kv_heads) * d * 4
+                + heads * d * 4)
+
+
+def run_attention(torch, bl, dev):
+    """bitlinear_attention_decode at the 2B (20 query / 5 KV heads) and 100B (64 / 8) head
+    shapes, every sequence at position ctx - 1, rotating cache copies (>= 1 GB) so that the
+    keys and values stream from HBM."""
+    out = {}
+    for tag, H, KVH, ctx, M in (("2B", 20, 5, 4096, 1), ("2B", 20, 5, 4096, 8), ("2B", 20, 5, 32768, 1),
+                                ("100B", 64, 8, 4096, 1)):
+        shape = (M, KVH, ctx, 128)
+        cache_bytes = 2 * M * KVH * ctx * 128 * 2
+        C = n_copies(cache_bytes)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(ctx + H)
+        kcs = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(C)]
+        vcs = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(C)]
+        qkv = torch.randn((M, (H + 2 * KVH) * 128), generator=gen, device=dev)
+        pos = torch.full((M,), ctx - 1, dtype=torch.int32, device=dev)
+        o = torch.empty((M, H * 128), dtype=torch.float32, device=dev)
+        ws = torch.empty((bl.bitlinear_attention_workspace_bytes(M, H, ctx),), dtype=torch.uint8, device=dev)
+        t = time_kernel(torch, lambda c: bl.bitlinear_attention_decode(qkv, kcs[c], vcs[c], pos, H, KVH, out=o,
+                                                                       workspace=ws), C, 100)
+        b = attention_bytes(M, H, KVH, ctx)
+        out["%s_ctx%d_M%d" % (tag, ctx, M)] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                                               "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                                               "algorithmic_MB": round(b / 1e6, 2), "finite": bool(torch.isfinite(o).all())}
+        del kcs, vcs
+        torch.cuda.empty_cache()
+    log("extra attention: %s" % out)
+    return out
+
+
+def run_stack(torch, bl, datagen, dev, gated, ctx=1, n_layers=30, copies=2, replays=20):
+    """Per-token latency of a 30-layer decode stack (one launch per BitLinear plus the two
+    attention launches) at position ctx - 1 (attending over ctx cached positions), as a HIP
+    graph over `copies` weight copies of the stack so that each pass streams its weights
+    (and caches) from HBM (>= 776 MB against 256 MB of MALL)."""
     from ternary_weight_linear_w1_amd.decode_stack import DecodeStack, LayerWeights
     d = STACK_DIMS
     H, F = d["hidden"], d["ffn"]
@@ -573,8 +618,13 @@ def run_stack(torch, bl, datagen, dev, gated, n_layers=30, copies=2, replays=20)
     for c in range(copies):
         layers = [LayerWeights(*[(m[n][0] if c == 0 else m[n][0].clone(), m[n][1]) for n in ("qkv", "o", "up", "down")],
                                **g) for m, g in base]
-        st = DecodeStack(layers, H, d["heads"], d["kv_heads"], d["head_dim"], F, gated, M=1, eps=EPS, device=dev)
+        st = DecodeStack(layers, H, d["heads"], d["kv_heads"], d["head_dim"], F, gated, M=1, eps=EPS, device=dev,
+                         capacity=max(ctx, 64))
         st.h.copy_(datagen.outlier_acts_torch(1, H, datagen.stream_id(3, 200, c, 1), dev))
+        st.pos.fill_(ctx - 1)
+        for li in range(n_layers):      # prior context: keys and values of unit scale
+            st.k_cache[li].normal_()
+            st.v_cache[li].normal_()
         stacks.append(st)
     for st in stacks:
         st.step()
@@ -593,13 +643,14 @@ def run_stack(torch, bl, datagen, dev, gated, n_layers=30, copies=2, replays=20)
     torch.cuda.synchronize()
     per_token = e0.elapsed_time(e1) * 1e-3 / (replays * copies)
     finite = all(bool(torch.isfinite(st.h).all()) for st in stacks)
-    nbytes = n_layers * sum(layer_bytes(N, K, 1, mode, residual=res) for _, N, K, mode, res in shapes)
+    nbytes = n_layers * (sum(layer_bytes(N, K, 1, mode, residual=res) for _, N, K, mode, res in shapes)
+                         + attention_bytes(1, d["heads"], d["kv_heads"], ctx))
     packed = n_layers * sum(N * K // 4 for _, N, K, _, _ in shapes)
     out = {"us_per_token": round(per_token * 1e6, 1), "GB/s": round(nbytes / per_token / 1e9, 1),
            "frac_hbm": round(nbytes / per_token / 1e9 / HBM_PEAK_GBS, 4), "packed_MB": round(packed / 1e6, 1),
-           "algorithmic_MB": round(nbytes / 1e6, 1), "launches_per_token": 5 * n_layers,
+           "algorithmic_MB": round(nbytes / 1e6, 1), "launches_per_token": 6 * n_layers, "context": ctx,
            "ideal_us_at_8TBs": round(nbytes / HBM_PEAK_GBS / 1e3, 1), "h_finite": finite}
-    log("extra stack%s: %s" % (" gated" if gated else "", out))
+    log("extra stack%s ctx %d: %s" % (" gated" if gated else "", ctx, out))
     del g, stacks, base
     return out
 

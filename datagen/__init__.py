@@ -16,6 +16,9 @@ Distributions (the shapes and value mixes of the layers the pages describe):
 * ``heavy_channel_acts`` activations ~ N(0, 1), except ceil(0.01 K) channels (chosen by a
                         seeded permutation) that hold Student-t (nu = 3) draws.
 * ``gains``             RMSNorm gains ~ U(0.5, 1.5).
+* ``bf16_cache``        random bfloat16 bit patterns for a key/value cache: N(0, std^2)
+                        draws in binary32 with the low 16 bits dropped.
+* ``small_ints``        integers drawn uniformly from [lo, hi], as binary32.
 
 Host generators use numpy's PCG64 seeded through SeedSequence([BASE_SEED, stream]).
 ``*_torch`` variants draw the same distributions on a torch device (Philox) for
@@ -81,6 +84,16 @@ def heavy_channel_acts(m: int, k: int, stream: int, frac: float = 0.01, nu: floa
 def gains(k: int, stream: int) -> np.ndarray:
     g = rng(stream)
     return g.uniform(0.5, 1.5, size=k).astype(np.float32)
+
+
+def bf16_cache(shape, stream: int, std: float = 1.0) -> np.ndarray:
+    g = rng(stream)
+    x = (g.standard_normal(shape) * std).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def small_ints(shape, stream: int, lo: int, hi: int) -> np.ndarray:
+    return rng(stream).integers(lo, hi + 1, size=shape).astype(np.float32)
 
 
 # --------------------------------------------------------------------------------------

@@ -38,6 +38,7 @@ extern "C" {
 #endif
 
 #define BITLINEAR_MAX_K (1 << 20)
+#define BITLINEAR_MAX_CONTEXT (1 << 24)
 
 typedef enum {
     BITLINEAR_OK = 0,
@@ -174,6 +175,48 @@ int64_t bitlinear_packed5_row_bytes(int64_t K);
 int bitlinear_repack5(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W_packed5, hipStream_t stream);
 int bitlinear_forward5(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed5,
                        const float* gamma, int64_t N, float* Y, int32_t* acc, hipStream_t stream);
+
+/*
+ * Decode attention at real context length: one new token per sequence attends over its
+ * key/value cache. Scaled dot-product attention ("BitNet b1.58 深度解析" s.2.4 block
+ * diagram, between the Q/K/V and output BitLinears) with rotary position embedding
+ * ("微软AI大模型炸场" s.2, 特殊设计) and grouped-query heads: query head h reads KV head
+ * h / (heads / kv_heads). The pages fix neither the rotary layout nor the cache format;
+ * this library rotates dimension i with dimension i + head_dim/2 by the angle
+ * pos * theta^(-2i/head_dim) and stores keys and values as bfloat16.
+ *
+ *   qkv       fp32 [M][(heads + 2 kv_heads) * head_dim]: the new token's query heads,
+ *             then key heads, then value heads (the Q/K/V BitLinear's output); read only
+ *   k_cache   bf16 bit patterns [M][kv_heads][capacity][head_dim]: rotated keys; slot
+ *   v_cache   pos[t] of sequence t is written, slots 0 .. pos[t]-1 are read, the others
+ *             are neither read nor written
+ *   pos       int32 [M] on the device: the new token's position per sequence
+ *   out       fp32 [M][heads * head_dim] (written)
+ *   workspace device scratch of at least bitlinear_attention_workspace_bytes(M, heads,
+ *             capacity) bytes, 16-byte aligned, contents undefined afterwards; concurrent
+ *             calls need distinct workspaces
+ *
+ * For each sequence t with 0 <= p = pos[t] < capacity:
+ *   k' = rotate(k, p) in binary32: cos and sin of the binary64 angle rounded once to
+ *        binary32, then x1*c - x2*s and x2*c + x1*s with each product and sum rounded;
+ *   k_cache[t][g][p] = bf16(k'_g), v_cache[t][g][p] = bf16(v_g) (nearest, ties to even);
+ *   out[t][h] = sum_{j<=p} softmax_j(rotate(q_h, p) . K[j] / sqrt(head_dim)) V[j] over
+ *        the cache rows of KV head g(h) (in fp32, weights as exp2 of base-2 scores).
+ * A sequence whose pos lies outside [0, capacity) gets NaN outputs and its caches are left
+ * untouched (pos is read on the device, so this is not an error status).
+ *
+ * Requirements: head_dim == 128; heads a multiple of kv_heads, heads <= 4096;
+ * 1 <= M <= 65535; 1 <= capacity <= BITLINEAR_MAX_CONTEXT; theta > 0 and finite; every
+ * pointer 16-byte aligned (pos 4-byte). No written buffer (caches, out, workspace) may
+ * overlap any other argument buffer. Three kernels are enqueued on `stream` (rotate and
+ * append; attend over 64-position chunks; merge the chunks).
+ * bitlinear_attention_workspace_bytes returns 0 for out-of-range sizes.
+ */
+size_t bitlinear_attention_workspace_bytes(int64_t M, int64_t heads, int64_t capacity);
+int bitlinear_attention_decode(const float* qkv, uint16_t* k_cache, uint16_t* v_cache, const int32_t* pos,
+                               int64_t M, int64_t heads, int64_t kv_heads, int64_t head_dim, int64_t capacity,
+                               double theta, float* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,8 @@ from ._build import LIB as _LIB_PATH
 
 __all__ = [
     "BitLinearError", "lib", "status_string", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
-    "bitlinear_quantize_act", "bitlinear_forward", "bitlinear_forward_f32", "EXPORTED",
+    "bitlinear_quantize_act", "bitlinear_forward", "bitlinear_forward_f32", "bitlinear_attention_workspace_bytes",
+    "bitlinear_attention_decode", "EXPORTED",
 ]
 
 EXPORTED = (
@@ -32,6 +33,8 @@ EXPORTED = (
     "bitlinear_packed5_row_bytes",
     "bitlinear_repack5",
     "bitlinear_forward5",
+    "bitlinear_attention_workspace_bytes",
+    "bitlinear_attention_decode",
 )
 
 _lib = None
@@ -73,6 +76,11 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_repack5.restype = ci
         L.bitlinear_forward5.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, vp]
         L.bitlinear_forward5.restype = ci
+        L.bitlinear_attention_workspace_bytes.argtypes = [i64, i64, i64]
+        L.bitlinear_attention_workspace_bytes.restype = ctypes.c_size_t
+        L.bitlinear_attention_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_double, vp, vp,
+                                                 ctypes.c_size_t, vp]
+        L.bitlinear_attention_decode.restype = ci
         _lib = L
     return _lib
 
@@ -271,3 +279,41 @@ def bitlinear_forward5(Xq, x_scale, W_packed5, gamma, y=None, acc=None, stream=N
                                     _ptr(acc if isinstance(acc, torch.Tensor) else None), _stream(stream)),
            "bitlinear_forward5")
     return (y, acc) if isinstance(acc, torch.Tensor) else y
+
+
+def bitlinear_attention_workspace_bytes(M: int, heads: int, capacity: int) -> int:
+    return int(lib().bitlinear_attention_workspace_bytes(int(M), int(heads), int(capacity)))
+
+
+def bitlinear_attention_decode(qkv, k_cache, v_cache, pos, heads: int, kv_heads: int, theta: float = 10000.0,
+                               out=None, workspace=None, stream=None):
+    """Decode attention of one new token per sequence over its bf16 key/value cache
+    (rotary positions, grouped-query heads, head_dim 128).
+
+    qkv fp32 [M][(heads + 2 kv_heads) * 128]; k_cache, v_cache bfloat16
+    [M][kv_heads][capacity][128] (slot pos[t] is written); pos int32 [M] on the device.
+    Returns out fp32 [M][heads * 128]. ``workspace`` (uint8, at least
+    bitlinear_attention_workspace_bytes bytes) is allocated when not given."""
+    import torch
+    _need(qkv, torch.float32, "qkv", 2)
+    M = qkv.shape[0]
+    _need(k_cache, torch.bfloat16, "k_cache", 4)
+    d = 128
+    capacity = k_cache.shape[2]
+    _need(qkv, torch.float32, "qkv", shape=(M, (heads + 2 * kv_heads) * d))
+    _need(k_cache, torch.bfloat16, "k_cache", shape=(M, kv_heads, capacity, d))
+    _need(v_cache, torch.bfloat16, "v_cache", shape=(M, kv_heads, capacity, d))
+    _need(pos, torch.int32, "pos", shape=(M,))
+    if out is None:
+        out = torch.empty((M, heads * d), dtype=torch.float32, device=qkv.device)
+    _need(out, torch.float32, "out", shape=(M, heads * d))
+    need = bitlinear_attention_workspace_bytes(M, heads, capacity)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=qkv.device)
+    _need(workspace, torch.uint8, "workspace", 1)
+    _check(lib().bitlinear_attention_decode(_ptr(qkv), _ptr(k_cache), _ptr(v_cache), _ptr(pos), M, int(heads),
+                                            int(kv_heads), d, capacity, float(theta), _ptr(out), _ptr(workspace),
+                                            workspace.numel(), _stream(stream)),
+           "bitlinear_attention_decode")
+    return out
+

@@ -1,0 +1,452 @@
+// attention.hpp -- decode attention at real context length (gfx950, wave64).
+//
+// One new token per sequence attends over its key/value cache: scaled dot-product
+// attention ("BitNet b1.58 深度解析" s.2.4 block diagram) with rotary position embedding
+// ("微软AI大模型炸场" s.2, 特殊设计), grouped-query heads (query head h reads KV head
+// h / (H / KVH)), head dimension 128, bf16 cache [M][KVH][C][128].
+//
+// The work is HBM-bound (every cached key and value is read once per step, for all the
+// query heads of its group), so the kernels are built for streaming, not for MFMA:
+//
+//   attn_rotate_kernel  one block per sequence. Lane i owns rotation pair (i, i + 64), so
+//                       each lane needs one angle: pos * theta^(-2i/128) in binary64, cos
+//                       and sin rounded once to binary32. Writes the rotated query heads,
+//                       pre-scaled by log2(e)/sqrt(128), to the workspace, and appends the
+//                       rotated key (binary32, no fused multiply-add: its bf16 rounding is a
+//                       decision) and the value, both rounded to bf16, at slot pos.
+//   attn_chunk_kernel   one block per (span of 64-position sub-chunks, group of GB query
+//                       heads of one KV head, sequence). A row of 16 lanes holds one cached
+//                       position (8 dims of 16 bytes per lane, so a wave reads 4 consecutive
+//                       rows = 1 KB contiguous); a sub-chunk's keys and values are all
+//                       requested before any arithmetic. Scores are reduced across the row
+//                       with DPP, the block maximum through LDS, and the block writes its
+//                       partial softmax state (max m, sum l, unnormalised sum acc of
+//                       weighted values) per head to the workspace. For short work the
+//                       kernel also does the rotation itself (ROT) and the rotate launch
+//                       is skipped.
+//   attn_combine_kernel one block per (head, sequence) merges the chunk partials:
+//                       out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, eight chunk
+//                       groups of 32 lanes (float4 each) with all loads in flight, then a
+//                       fixed-order sum over the groups.
+//
+// Scores are kept in base 2, so weights are exp2 of differences. Every reduction follows
+// a fixed order, so results do not depend on timing.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace bl {
+
+constexpr int kAttnD = 128;      // head dimension
+constexpr int kAttnChunk = 64;   // positions per block: 4 waves x 4 rows x 4 iterations
+constexpr int kAttnIter = 4;
+
+struct AttnArgs {
+    const float* qkv;     // [M][(H + 2 KVH) * 128]: query heads, key heads, value heads
+    uint16_t* kc;         // bf16 [M][KVH][C][128]
+    uint16_t* vc;         // bf16 [M][KVH][C][128]
+    const int* pos;       // [M]
+    float* out;           // [M][H * 128]
+    float* part_acc;      // [M][H][S][128]
+    float* part_ml;       // [M][H][S][2]: block max (base 2), block sum
+    float* qr;            // [M][H][128]: rotated, pre-scaled queries
+    int H, KVH, C, S;     // S = ceil(C / 64): partial slots per (sequence, head)
+    int cpb;              // 64-position sub-chunks per chunk block
+    double theta;         // rotary base
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
+
+// Round a finite binary32 value to bfloat16, nearest with ties to even.
+__device__ __forceinline__ uint32_t f32_to_bf16(float v)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float row_sum16(float v)
+{
+    v = v + dpp_f32<0xB1>(v);
+    v = v + dpp_f32<0x4E>(v);
+    v = v + dpp_f32<0x141>(v);
+    v = v + dpp_f32<0x140>(v);
+    return v;
+}
+
+__device__ __forceinline__ float lane_f(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+constexpr float kQScale = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
+
+__global__ __launch_bounds__(256) void attn_rotate_kernel(AttnArgs a)
+{
+    const int b = blockIdx.x, w = threadIdx.x >> 6, i = threadIdx.x & 63;
+    const int p = a.pos[b];
+    if (p < 0 || p >= a.C)
+        return;
+    const double ang = (double)p * pow(a.theta, -(2.0 * i) / (double)kAttnD);
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    const float c = (float)cd, s = (float)sd;
+    const float* row = a.qkv + (size_t)b * (a.H + 2 * a.KVH) * kAttnD;
+    // query heads: rotated and pre-scaled (not a rounding decision)
+    for (int h = w; h < a.H; h += 4) {
+        const float x1 = row[h * kAttnD + i], x2 = row[h * kAttnD + i + kAttnD / 2];
+        float* q = a.qr + ((size_t)b * a.H + h) * kAttnD;
+        q[i] = (x1 * c - x2 * s) * kQScale;
+        q[i + kAttnD / 2] = (x2 * c + x1 * s) * kQScale;
+    }
+    // key heads: rotated with every product and sum rounded, then bf16; value heads: bf16
+    for (int g = w; g < a.KVH; g += 4) {
+        const float* kr = row + (a.H + g) * kAttnD;
+        const float* vr = row + (a.H + a.KVH + g) * kAttnD;
+        const float x1 = kr[i], x2 = kr[i + kAttnD / 2];
+        const float lo = __fsub_rn(__fmul_rn(x1, c), __fmul_rn(x2, s));
+        const float hi = __fadd_rn(__fmul_rn(x2, c), __fmul_rn(x1, s));
+        const size_t slot = (((size_t)b * a.KVH + g) * a.C + p) * kAttnD;
+        a.kc[slot + i] = (uint16_t)f32_to_bf16(lo);
+        a.kc[slot + i + kAttnD / 2] = (uint16_t)f32_to_bf16(hi);
+        a.vc[slot + i] = (uint16_t)f32_to_bf16(vr[i]);
+        a.vc[slot + i + kAttnD / 2] = (uint16_t)f32_to_bf16(vr[i + kAttnD / 2]);
+    }
+}
+
+// One block per (span of `cpb` 64-position sub-chunks, group of GB query heads of one KV
+// head, sequence). Per sub-chunk: request its keys and values, score them, take the
+// block maximum (LDS, one barrier), rescale the running sums to the new maximum and add
+// the sub-chunk's weighted values. Every row of the block uses the same running maximum,
+// so the final sum over rows needs no rescaling.
+//
+// Two forms. LOOP = false (one sub-chunk per block, cpb == 1): the kernel rotates the
+// queries itself (each wave builds the 64-angle table while its key/value loads are in
+// flight) and the block owning position pos appends the new key and value, so no rotate
+// launch is needed; there is no running state. LOOP = true (cpb >= 1): the queries come
+// pre-rotated from attn_rotate_kernel and the running sums are rescaled per sub-chunk.
+template <int GB, bool LOOP>
+__global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a)
+{
+    constexpr bool ROT = !LOOP;
+    __shared__ float2 rot[ROT ? 4 : 1][64];        // per-wave (cos, sin) of the 64 pair angles
+    __shared__ float wmax[2][4][GB];               // per-wave sub-chunk maxima, by parity
+    __shared__ float4 red[4 * 4][GB][kAttnD / 4];  // per-row partial acc
+    __shared__ float redl[4 * 4][GB];
+
+    const int c = blockIdx.x, gi = blockIdx.y, b = blockIdx.z;
+    const int G = a.H / a.KVH, per = G / GB;
+    const int kh = gi / per, h0 = kh * G + (gi - kh * per) * GB;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane >> 4, t = lane & 15;
+    const int d0 = 8 * t;                          // this lane's 8 dims
+    const int dp = (d0 + kAttnD / 2) & (kAttnD - 1);  // the rotation partner's 8 dims
+
+    // Query values first: they do not depend on pos, and loads complete in order, so they
+    // must not queue behind the keys and values.
+    float q[GB][8], yv[ROT ? GB : 1][8];
+    const float* qrow = a.qkv + (size_t)b * (a.H + 2 * a.KVH) * kAttnD;
+#pragma unroll
+    for (int hh = 0; hh < GB; ++hh) {
+        const float* src = ROT ? qrow + (h0 + hh) * kAttnD + d0 : a.qr + ((size_t)b * a.H + h0 + hh) * kAttnD + d0;
+        const float4 x0 = reinterpret_cast<const float4*>(src)[0], x1 = reinterpret_cast<const float4*>(src)[1];
+        q[hh][0] = x0.x; q[hh][1] = x0.y; q[hh][2] = x0.z; q[hh][3] = x0.w;
+        q[hh][4] = x1.x; q[hh][5] = x1.y; q[hh][6] = x1.z; q[hh][7] = x1.w;
+        if constexpr (ROT) {
+            const float4* y = reinterpret_cast<const float4*>(qrow + (h0 + hh) * kAttnD + dp);
+            const float4 y0 = y[0], y1 = y[1];
+            yv[hh][0] = y0.x; yv[hh][1] = y0.y; yv[hh][2] = y0.z; yv[hh][3] = y0.w;
+            yv[hh][4] = y1.x; yv[hh][5] = y1.y; yv[hh][6] = y1.z; yv[hh][7] = y1.w;
+        }
+    }
+
+    const int p = a.pos[b];
+    const int sc0 = c * a.cpb;                     // first sub-chunk of this block
+    if (p < 0 || p >= a.C || sc0 * kAttnChunk > p)
+        return;
+    const int sc1 = min(sc0 + a.cpb, p / kAttnChunk + 1);
+    // slot p is read from the cache when the rotate kernel appended it; with ROT it comes
+    // from registers
+    const int jlast = ROT ? p - 1 : p;
+    const size_t row0 = ((size_t)b * a.KVH + kh) * (size_t)a.C;
+
+    // all keys of a sub-chunk first, then its values: scoring waits only for the keys
+    uint4 kr[kAttnIter], vr[kAttnIter];
+    int jj[kAttnIter];
+    auto issue = [&](int sc) {
+#pragma unroll
+        for (int it = 0; it < kAttnIter; ++it) {
+            const int j = sc * kAttnChunk + (it * 4 + w) * 4 + r;
+            jj[it] = j;
+            kr[it] = make_uint4(0, 0, 0, 0);
+            if (j <= jlast)
+                kr[it] = *(const uint4*)(a.kc + (row0 + j) * kAttnD + d0);
+        }
+#pragma unroll
+        for (int it = 0; it < kAttnIter; ++it) {
+            vr[it] = make_uint4(0, 0, 0, 0);
+            if (jj[it] <= jlast)
+                vr[it] = *(const uint4*)(a.vc + (row0 + jj[it]) * kAttnD + d0);
+        }
+    };
+    issue(sc0);
+
+    // Rotated, pre-scaled queries of the block's heads (this lane's 8 dims).
+    uint4 kn = make_uint4(0, 0, 0, 0), vn = make_uint4(0, 0, 0, 0);
+    const bool own = ROT && p / kAttnChunk < sc1;  // this block holds position p
+    if constexpr (ROT) {
+        {
+            const double ang = (double)p * pow(a.theta, -(2.0 * lane) / (double)kAttnD);
+            double sd, cd;
+            sincos(ang, &sd, &cd);
+            rot[w][lane] = make_float2((float)cd, (float)sd);
+        }
+        // the table is private to the wave: a wave-scope release/acquire orders it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float cs[8], sn[8];
+        const float4* tp = reinterpret_cast<const float4*>(&rot[w][d0 & 63]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float4 v = tp[e];
+            cs[2 * e] = v.x; sn[2 * e] = v.y; cs[2 * e + 1] = v.z; sn[2 * e + 1] = v.w;
+        }
+        const bool hi = t >= 8;   // second half of the head: x2*c + x1*s
+#pragma unroll
+        for (int hh = 0; hh < GB; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float rv = hi ? q[hh][e] * cs[e] + yv[hh][e] * sn[e] : q[hh][e] * cs[e] - yv[hh][e] * sn[e];
+                q[hh][e] = rv * kQScale;
+            }
+        // the new key: every product and sum rounded (its bf16 rounding is a decision)
+        if (own) {
+            const float* krow = qrow + (a.H + kh) * kAttnD;
+            const float* vrow = qrow + (a.H + a.KVH + kh) * kAttnD;
+            uint32_t kb[8], vb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = krow[d0 + e], y = krow[dp + e];
+                const float rv = hi ? __fadd_rn(__fmul_rn(x, cs[e]), __fmul_rn(y, sn[e]))
+                                    : __fsub_rn(__fmul_rn(x, cs[e]), __fmul_rn(y, sn[e]));
+                kb[e] = f32_to_bf16(rv);
+                vb[e] = f32_to_bf16(vrow[d0 + e]);
+            }
+            kn = make_uint4(kb[0] | kb[1] << 16, kb[2] | kb[3] << 16, kb[4] | kb[5] << 16, kb[6] | kb[7] << 16);
+            vn = make_uint4(vb[0] | vb[1] << 16, vb[2] | vb[3] << 16, vb[4] | vb[5] << 16, vb[6] | vb[7] << 16);
+            if (gi - kh * per == 0 && w == 0 && r == 0) {   // append once per KV head
+                *(uint4*)(a.kc + (row0 + p) * kAttnD + d0) = kn;
+                *(uint4*)(a.vc + (row0 + p) * kAttnD + d0) = vn;
+            }
+        }
+    }
+
+    float mrun[GB], lrun[GB], acc[GB][8];
+#pragma unroll
+    for (int hh = 0; hh < GB; ++hh) {
+        mrun[hh] = -__builtin_huge_valf();
+        lrun[hh] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[hh][e] = 0.0f;
+    }
+    const int row = w * 4 + r;
+    const int scend = LOOP ? sc1 : sc0 + 1;     // without LOOP, cpb == 1
+    for (int sc = sc0; sc < scend; ++sc) {
+        if (sc != sc0)
+            issue(sc);
+        if (own) {
+#pragma unroll
+            for (int it = 0; it < kAttnIter; ++it)
+                if (jj[it] == p) {
+                    kr[it] = kn;
+                    vr[it] = vn;
+                }
+        }
+        // scores (base 2) of the lane's row positions, reduced across the row
+        float s[kAttnIter][GB];
+#pragma unroll
+        for (int it = 0; it < kAttnIter; ++it) {
+            const uint32_t kw[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
+            float kf[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kf[2 * e] = bf16_to_f32(kw[e] & 0xFFFFu);
+                kf[2 * e + 1] = bf16_to_f32(kw[e] >> 16);
+            }
+#pragma unroll
+            for (int hh = 0; hh < GB; ++hh) {
+                float d = q[hh][0] * kf[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e)
+                    d = __builtin_fmaf(q[hh][e], kf[e], d);
+                d = row_sum16(d);
+                s[it][hh] = jj[it] <= p ? d : -__builtin_huge_valf();
+            }
+        }
+        // sub-chunk maximum per head: the lane's positions, the wave's 4 rows, 4 waves
+        const int par = (sc - sc0) & 1;
+#pragma unroll
+        for (int hh = 0; hh < GB; ++hh) {
+            float m = s[0][hh];
+#pragma unroll
+            for (int it = 1; it < kAttnIter; ++it)
+                m = fmaxf(m, s[it][hh]);
+            m = fmaxf(fmaxf(lane_f(m, 0), lane_f(m, 16)), fmaxf(lane_f(m, 32), lane_f(m, 48)));
+            if (lane == 0)
+                wmax[par][w][hh] = m;
+        }
+        __syncthreads();
+        // rescale the running sums to the new maximum, then add this sub-chunk's weights
+#pragma unroll
+        for (int hh = 0; hh < GB; ++hh) {
+            const float msub = fmaxf(fmaxf(wmax[par][0][hh], wmax[par][1][hh]), fmaxf(wmax[par][2][hh], wmax[par][3][hh]));
+            const float mnew = LOOP ? fmaxf(mrun[hh], msub) : msub;
+            if constexpr (LOOP) {
+                const float scale = exp2f(mrun[hh] - mnew);    // 0 on the first sub-chunk
+                lrun[hh] *= scale;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[hh][e] *= scale;
+            }
+            mrun[hh] = mnew;
+            // without LOOP the head's sums go straight to LDS (no state across heads)
+            float a8[8], l = LOOP ? lrun[hh] : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                a8[e] = LOOP ? acc[hh][e] : 0.0f;
+#pragma unroll
+            for (int it = 0; it < kAttnIter; ++it) {
+                const float pw = exp2f(s[it][hh] - mnew);   // 0 for masked positions
+                l += pw;
+                if (jj[it] <= p) {
+                    const uint32_t vw[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        a8[2 * e] = __builtin_fmaf(pw, bf16_to_f32(vw[e] & 0xFFFFu), a8[2 * e]);
+                        a8[2 * e + 1] = __builtin_fmaf(pw, bf16_to_f32(vw[e] >> 16), a8[2 * e + 1]);
+                    }
+                }
+            }
+            if constexpr (LOOP) {
+                lrun[hh] = l;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[hh][e] = a8[e];
+            } else {
+                red[row][hh][2 * t] = make_float4(a8[0], a8[1], a8[2], a8[3]);
+                red[row][hh][2 * t + 1] = make_float4(a8[4], a8[5], a8[6], a8[7]);
+                if (t == 0)
+                    redl[row][hh] = l;
+            }
+        }
+    }
+
+    // Sum the 16 rows in order and write the block's partial state per head.
+    if constexpr (LOOP) {
+#pragma unroll
+        for (int hh = 0; hh < GB; ++hh) {
+            red[row][hh][2 * t] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+            red[row][hh][2 * t + 1] = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
+            if (t == 0)
+                redl[row][hh] = lrun[hh];
+        }
+    }
+    __syncthreads();
+    for (int o = tid; o < GB * kAttnD; o += 256) {
+        const int hh = o / kAttnD, d = o - hh * kAttnD;
+        const float* rp = reinterpret_cast<const float*>(&red[0][hh][0]) + d;
+        float sum = 0.0f;
+#pragma unroll
+        for (int q16 = 0; q16 < 16; ++q16)
+            sum += rp[(size_t)q16 * GB * kAttnD];
+        const size_t rec = ((size_t)b * a.H + h0 + hh) * a.S + c;
+        a.part_acc[rec * kAttnD + d] = sum;
+        if (d == 0) {
+            float l = 0.0f;
+#pragma unroll
+            for (int q16 = 0; q16 < 16; ++q16)
+                l += redl[q16][hh];
+            // every thread holds the same running maximum; pick it without dynamic indexing
+            float m = mrun[0];
+#pragma unroll
+            for (int x = 1; x < GB; ++x)
+                m = hh == x ? mrun[x] : m;
+            a.part_ml[rec * 2] = m;
+            a.part_ml[rec * 2 + 1] = l;
+        }
+    }
+}
+
+// One block per (head, sequence): thread (g, q) with g = tid / 32 (chunk group) and
+// q = tid % 32 (dims 4q .. 4q+3) sums chunks g, g + 8, g + 16, ...
+constexpr int kCombUnroll = 8;
+
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
+{
+    __shared__ float gmax[4];
+    __shared__ float4 red[8][kAttnD / 4];
+    __shared__ float redl[8];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, g = tid >> 5, q = tid & 31;
+    const int p = a.pos[b];
+    float* o = a.out + ((size_t)b * a.H + h) * kAttnD;
+    if (p < 0 || p >= a.C) {
+        if (tid < kAttnD)
+            o[tid] = __builtin_nanf("");
+        return;
+    }
+    const int n = p / (kAttnChunk * a.cpb) + 1;   // live chunk blocks
+    const size_t rec0 = ((size_t)b * a.H + h) * a.S;
+    const float* ml = a.part_ml + rec0 * 2;
+    // maximum of the chunk maxima (order-free)
+    float m = -__builtin_huge_valf();
+    for (int c = tid; c < n; c += 256)
+        m = fmaxf(m, ml[2 * c]);
+    m = wave_max(m);
+    if ((tid & 63) == 0)
+        gmax[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(gmax[0], gmax[1]), fmaxf(gmax[2], gmax[3]));
+    // this thread's chunks, kCombUnroll loads in flight at a time
+    const float4* pa = reinterpret_cast<const float4*>(a.part_acc + rec0 * kAttnD) + q;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float l = 0.0f;
+    for (int c0 = g; c0 < n; c0 += 8 * kCombUnroll) {
+        float4 v[kCombUnroll];
+        float2 mlv[kCombUnroll];
+#pragma unroll
+        for (int u = 0; u < kCombUnroll; ++u) {
+            const int c = c0 + 8 * u;
+            v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            mlv[u] = make_float2(-__builtin_huge_valf(), 0.0f);
+            if (c < n) {
+                v[u] = pa[(size_t)c * (kAttnD / 4)];
+                mlv[u] = *reinterpret_cast<const float2*>(ml + 2 * c);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCombUnroll; ++u) {
+            const float wgt = exp2f(mlv[u].x - m);     // 0 past n
+            l = __builtin_fmaf(wgt, mlv[u].y, l);
+            acc.x = __builtin_fmaf(wgt, v[u].x, acc.x);
+            acc.y = __builtin_fmaf(wgt, v[u].y, acc.y);
+            acc.z = __builtin_fmaf(wgt, v[u].z, acc.z);
+            acc.w = __builtin_fmaf(wgt, v[u].w, acc.w);
+        }
+    }
+    red[g][q] = acc;
+    if (q == 0)
+        redl[g] = l;
+    __syncthreads();
+    if (tid < kAttnD) {
+        const float* rp = reinterpret_cast<const float*>(&red[0][0]) + tid;
+        float sum = 0.0f, lsum = 0.0f;
+#pragma unroll
+        for (int gg = 0; gg < 8; ++gg) {
+            sum += rp[gg * kAttnD];
+            lsum += redl[gg];
+        }
+        o[tid] = sum / lsum;
+    }
+}
+
+}  // namespace bl

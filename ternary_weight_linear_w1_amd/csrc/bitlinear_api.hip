@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "../../include/bitlinear.h"
+#include "attention.hpp"
 #include "device_common.hpp"
 #include "gemm.hpp"
 #include "gemv.hpp"
@@ -406,6 +407,17 @@ void dispatch5(const bl::Fwd5Args& a, hipStream_t stream)
     launch5<256, 1, 8>(a, stream);
 }
 
+// Decode attention: bytes of the chunk partials (acc [M][H][S][128] then (m, l) pairs).
+int64_t attn_chunks(int64_t capacity) { return (capacity + bl::kAttnChunk - 1) / bl::kAttnChunk; }
+
+template <int GB, bool LOOP>
+void launch_attn(const bl::AttnArgs& a, int M, hipStream_t stream)
+{
+    const int G = a.H / a.KVH;
+    const dim3 grid((unsigned)((a.S + a.cpb - 1) / a.cpb), (unsigned)(a.KVH * (G / GB)), (unsigned)M);
+    hipLaunchKernelGGL((bl::attn_chunk_kernel<GB, LOOP>), grid, dim3(256), 0, stream, a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -577,6 +589,89 @@ int bitlinear_forward5(const int8_t* Xq, const float* x_scale, int64_t M, int64_
         return BITLINEAR_ERR_ALIAS;
     bl::Fwd5Args a{Xq, x_scale, W_packed5, gamma, Y, acc, M, N, (int)K, (int)rb};
     dispatch5(a, stream);
+    return launched();
+}
+
+size_t bitlinear_attention_workspace_bytes(int64_t M, int64_t heads, int64_t capacity)
+{
+    if (M < 1 || heads < 1 || capacity < 1 || M > 65535 || heads > 4096 || capacity > BITLINEAR_MAX_CONTEXT)
+        return 0;
+    // chunk partials acc [M][H][S][128], rotated queries [M][H][128], partials (m, l) [M][H][S][2]
+    return (size_t)(M * heads * (attn_chunks(capacity) * (bl::kAttnD + 2) + bl::kAttnD) * 4);
+}
+
+int bitlinear_attention_decode(const float* qkv, uint16_t* k_cache, uint16_t* v_cache, const int32_t* pos,
+                               int64_t M, int64_t heads, int64_t kv_heads, int64_t head_dim, int64_t capacity,
+                               double theta, float* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    if (!qkv || !k_cache || !v_cache || !pos || !out || !workspace)
+        return BITLINEAR_ERR_NULL;
+    if (M < 1 || M > 65535 || heads < 1 || heads > 4096 || kv_heads < 1 || heads % kv_heads != 0 ||
+        head_dim != bl::kAttnD || capacity < 1 || capacity > BITLINEAR_MAX_CONTEXT ||
+        M * kv_heads * capacity > kMaxElems / head_dim || !(theta > 0.0) || !(theta < 1e300))
+        return BITLINEAR_ERR_SHAPE;
+    const int64_t need = (int64_t)bitlinear_attention_workspace_bytes(M, heads, capacity);
+    if ((int64_t)workspace_bytes < need)
+        return BITLINEAR_ERR_WORKSPACE;
+    if (!aligned(qkv, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(pos, 4) ||
+        !aligned(out, 16) || !aligned(workspace, 16))
+        return BITLINEAR_ERR_ALIGN;
+    const int64_t cbytes = M * kv_heads * capacity * head_dim * 2;
+    const void* bufs[6] = {qkv, pos, k_cache, v_cache, out, workspace};
+    const int64_t sz[6] = {M * (heads + 2 * kv_heads) * head_dim * 4, M * 4, cbytes, cbytes, M * heads * head_dim * 4,
+                           need};
+    // written: the caches (2, 3), out (4) and the workspace (5); none may touch another buffer
+    for (int wi = 2; wi < 6; ++wi)
+        for (int i = 0; i < 6; ++i)
+            if (i != wi && overlap(bufs[wi], sz[wi], bufs[i], sz[i]))
+                return BITLINEAR_ERR_ALIAS;
+    const int64_t S = attn_chunks(capacity);
+    float* part_acc = static_cast<float*>(workspace);
+    float* qr = part_acc + M * heads * S * bl::kAttnD;
+    float* part_ml = qr + M * heads * bl::kAttnD;
+    // When one 64-position sub-chunk per block needs at most two blocks per compute unit,
+    // the chunk kernel also rotates and appends (no rotate launch). Else each block takes
+    // several sub-chunks (at most 4 query heads per block, which keeps the running state in
+    // registers) so that about four blocks per compute unit remain: measured on MI355X,
+    // three sub-chunks per block beat one (fewer partials to merge) and five or more (each
+    // sub-chunk waits a full memory round trip).
+    const int64_t G = heads / kv_heads;
+    const int64_t cus = cu_count();
+    const int GB1 = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+    const bool loop = S * kv_heads * (G / GB1) * M > 2 * cus;
+    int GB = GB1;
+    int64_t cpb = 1;
+    if (loop) {
+        GB = GB1 > 4 ? 4 : GB1;
+        cpb = (S * kv_heads * (G / GB) * M + 4 * cus - 1) / (4 * cus);
+    }
+    if (kv_heads * (G / GB) > 65535)
+        return BITLINEAR_ERR_SHAPE;
+    bl::AttnArgs a{qkv, k_cache, v_cache, pos, out, part_acc, part_ml, qr, (int)heads, (int)kv_heads, (int)capacity,
+                   (int)S, (int)(cpb < S ? cpb : S), theta};
+    int st = BITLINEAR_OK;
+    if (loop) {
+        hipLaunchKernelGGL(bl::attn_rotate_kernel, dim3((unsigned)M), dim3(256), 0, stream, a);
+        if ((st = launched()) != BITLINEAR_OK)
+            return st;
+        switch (GB) {
+        case 4: launch_attn<4, true>(a, (int)M, stream); break;
+        case 2: launch_attn<2, true>(a, (int)M, stream); break;
+        default: launch_attn<1, true>(a, (int)M, stream); break;
+        }
+    } else {
+        switch (GB) {
+        case 8: launch_attn<8, false>(a, (int)M, stream); break;
+        case 4: launch_attn<4, false>(a, (int)M, stream); break;
+        case 2: launch_attn<2, false>(a, (int)M, stream); break;
+        default: launch_attn<1, false>(a, (int)M, stream); break;
+        }
+    }
+    st = launched();
+    if (st != BITLINEAR_OK)
+        return st;
+    hipLaunchKernelGGL(bl::attn_combine_kernel, dim3((unsigned)heads, (unsigned)M), dim3(256), 0, stream, a);
     return launched();
 }
 

@@ -168,3 +168,47 @@ def test_five_per_byte_calls_reject_before_launch(L):
     assert f(*args(Xq=P(a + 4))) == ERR_ALIGN
     assert f(*args(W=P(3 * a + 4))) == ERR_ALIGN
     assert f(*args(Y=P(3 * a))) == ERR_ALIAS
+
+
+def test_attention_workspace_bytes(L):
+    # (M, heads, capacity) -> per (sequence, head): ceil(capacity / 64) chunk records of 128 + 2
+    # floats and the 128 rotated query values
+    for M, H, C in [(1, 20, 4096), (3, 64, 100), (1, 1, 1), (65535, 1, 64)]:
+        assert bl.bitlinear_attention_workspace_bytes(M, H, C) == M * H * ((-(-C // 64)) * 130 + 128) * 4
+    for bad in [(0, 20, 64), (1, 0, 64), (1, 20, 0), (65536, 1, 64), (1, 4097, 64), (1, 1, (1 << 24) + 1)]:
+        assert bl.bitlinear_attention_workspace_bytes(*bad) == 0
+
+
+def test_attention_rejects_before_launch(L):
+    A = 1 << 20
+    qkv, kc, vc, pos, out, ws = P(1 * A), P(64 * A), P(128 * A), P(192 * A), P(200 * A), P(256 * A)
+    need = bl.bitlinear_attention_workspace_bytes(1, 20, 4096)
+    f = L.bitlinear_attention_decode
+
+    def call(**kw):
+        a = dict(qkv=qkv, kc=kc, vc=vc, pos=pos, M=1, H=20, KVH=5, D=128, C=4096, theta=10000.0, out=out, ws=ws,
+                 wsb=need)
+        a.update(kw)
+        return f(a["qkv"], a["kc"], a["vc"], a["pos"], a["M"], a["H"], a["KVH"], a["D"], a["C"], a["theta"],
+                 a["out"], a["ws"], a["wsb"], None)
+
+    assert call(qkv=None) == ERR_NULL
+    assert call(pos=None) == ERR_NULL
+    assert call(ws=None) == ERR_NULL
+    assert call(D=64) == ERR_SHAPE
+    assert call(KVH=3) == ERR_SHAPE                 # 20 % 3 != 0
+    assert call(M=0) == ERR_SHAPE
+    assert call(M=65536) == ERR_SHAPE
+    assert call(C=0) == ERR_SHAPE
+    assert call(C=(1 << 24) + 1) == ERR_SHAPE
+    assert call(theta=0.0) == ERR_SHAPE
+    assert call(theta=float("nan")) == ERR_SHAPE
+    assert call(theta=float("inf")) == ERR_SHAPE
+    assert call(wsb=need - 1) == ERR_WORKSPACE
+    assert call(qkv=P(A + 4)) == ERR_ALIGN
+    assert call(kc=P(64 * A + 8)) == ERR_ALIGN
+    assert call(pos=P(192 * A + 2)) == ERR_ALIGN
+    assert call(out=P(qkv.value)) == ERR_ALIAS       # output on the input
+    assert call(vc=P(kc.value + 4096)) == ERR_ALIAS  # value cache inside the key cache
+    assert call(ws=P(out.value)) == ERR_ALIAS
+    assert call(pos=P(ws.value + 16)) == ERR_ALIAS   # device pos inside the workspace
