@@ -193,7 +193,7 @@ def read_traffic():
         return None
 
 
-def summarize_trace(trace_csv, stats_csv, out, command=None):
+def summarize_trace(trace_csv, stats_csv, out, command="--steps 80 --warmup 8 --no-extra --no-cpu-baseline"):
     """Per (kernel, grid) durations from a rocprofv3 kernel trace (End - Start per
     dispatch) and the library rows of its stats table, as text for profiles/."""
     import csv
@@ -212,9 +212,10 @@ def summarize_trace(trace_csv, stats_csv, out, command=None):
         f.write("# rocprofv3 kernel trace of bench.py (library kernels; durations End - Start per dispatch, us)\n")
         f.write("# command (GPU box, repository root in $R):\n")
         f.write("#   cd /tmp && rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof_bench -o trace "
-                "--output-format csv -- python3 $R/bench.py --steps 80 --warmup 8 --no-extra --no-cpu-baseline\n")
-        f.write("#   python3 bench.py --summarize-trace <trace_kernel_trace.csv> <trace_kernel_stats.csv> <this file>\n")
-        f.write("# WGs = grid X / 256 (work-groups per launch row), gridY = token tiles\n#\n")
+                "--output-format csv -- python3 $R/bench.py %s\n" % command)
+        f.write("#   python3 bench.py --summarize-trace <trace_kernel_trace.csv> <trace_kernel_stats.csv> <this file>%s\n"
+                % ("" if command.startswith("--steps 80") else " --trace-command=%s" % command))
+        f.write("# WGs = grid X / 256 (work-groups per launch row), gridY = grid Y (token tiles; attention: head groups)\n#\n")
         f.write("# %-48s %5s %5s %5s %6s %6s %8s %8s %8s\n" % ("kernel", "WGs", "gridY", "VGPR", "LDS", "calls", "avg_us",
                                                             "med_us", "min_us"))
         for key in sorted(rows):
@@ -291,15 +292,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--profile", choices=["none", "roofline"], default="none")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary configurations")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="time only the decode-attention cases (a short program for kernel traces)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "STATS_CSV", "OUT"))
+    ap.add_argument("--trace-command", default="--steps 80 --warmup 8 --no-extra --no-cpu-baseline",
+                    help="bench.py arguments of the traced run (written into the summary)")
     ap.add_argument("--copy-bytes", type=int, default=256 << 20)
     args = ap.parse_args()
 
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace)
+        summarize_trace(*args.summarize_trace, command=args.trace_command)
         return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_bytes, TRAFFIC_FILE)
@@ -322,6 +327,9 @@ def main():
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.attention_only:
+        print(json.dumps({"attention_decode": run_attention(torch, bl, dev)}))
+        return 0
 
     # ---- the 2B layer at M = 1
     layer_copy_bytes = sum(N * K // 4 for _, N, K, _ in LAYER_2B)
