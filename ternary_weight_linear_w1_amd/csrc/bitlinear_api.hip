@@ -234,14 +234,16 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
     if (((a.M + 31) / 32) * ((a.N + 127) / 128) >= INT32_MAX)
         return false;
     // Tile shapes from timing the 2B prefill (M = 512, 2048) and 100B (M = 64) shapes: the
-    // 64 x 256 tile (K steps of 128) is faster per tile, but a launch that leaves most of
-    // its last round of resident blocks empty loses to 32 x 128 tiles (K steps of 256).
+    // 64 x 256 tile (K steps of 128) is faster per tile, but a launch that fills less than
+    // three quarters of its rounds of resident blocks loses to 32 x 128 tiles (K steps of
+    // 256): at M = 2048 on MI355X, QKV (480 tiles, 94% of 512 slots) and up (84%) take the
+    // big tile, O and down (320 tiles, 62%) the small one.
     if (a.M >= 1024) {
         const int64_t tiles = ((a.M + 63) / 64) * ((a.N + 255) / 256);
         const int64_t slots = int64_t(cu_count()) *
                               resident_blocks(bl::gemm_mfma_kernel<64, 256, 1, 4, 2, false, 128>, g_occ_gemm_big);
         const int64_t rounds = (tiles + slots - 1) / slots;
-        if (2 * tiles >= rounds * slots) {
+        if (4 * tiles >= 3 * rounds * slots) {
             launch_gemm<64, 256, 1, 4, 2, 128>(a, stream);
             return true;
         }

@@ -139,15 +139,16 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
             for (int h = 0; h < BH; ++h)
                 bd[fn][h] = buf_load16(rb, boff[fn], (k0 >> 2) + 32 * h);
     };
-    // The last step may extend past K (K % BK is a multiple of 64): data loaded from
-    // beyond the row end belongs to the next row and is replaced by zeros.
-    auto store_a = [&](const u32x4 (&src)[AU], int buf, int kvalid) {
+    // The last step may extend past K (K % BK is a multiple of 64): activations loaded
+    // from beyond the row end belong to the next row and are replaced by zeros, which also
+    // zeroes those columns' products whatever the weight bytes there hold.
+    auto store_a = [&](const u32x4 (&src)[AU], int buf, int kvalid, bool tail) {
 #pragma unroll
         for (int i = 0; i < AU; ++i) {
             const int u = tid + 256 * i;
             const int r = u / UPR, c = u % UPR;
             u32x4 v = src[i];
-            if (acol >= kvalid)
+            if (tail && acol >= kvalid)   // `tail` is a constant after inlining
                 v = u32x4{0u, 0u, 0u, 0u};
             uint32_t o[4];
             transpose_bytes(v[0], v[1], v[2], v[3], o);
@@ -172,72 +173,79 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
     for (int s = 0; s < P; ++s)
         if (s < nk)
             load(areg[s], breg[s], s * SK);
-    store_a(areg[0], 0, K);
+    store_a(areg[0], 0, K, true);
     __syncthreads();
 
-    for (int it0 = 0; it0 < nk; it0 += P) {
+    // One K step on ring slot s: unpack its weights (the slot is refilled right after),
+    // read the activation fragments, run the 4 * FM * FN matrix instructions, stage the
+    // next step's activations into the other LDS buffer.
+    auto step = [&](int it, int s, bool reload, bool stage, bool tail) {
+        // Keep each step's instructions inside the step: hoisting the next step's unpack
+        // would make it wait for the newest loads and raise the register count.
+        __builtin_amdgcn_sched_barrier(0);
+        const int buf = it & 1;
+        // Weight bytes past the row end need no mask (the activations there are 0).
+        v4i bf[KS][FN];
 #pragma unroll
-        for (int s = 0; s < P; ++s) {
-            const int it = it0 + s;
-            if (it < nk) {
-                const int buf = it & 1;
-                const int kvalid = K - it * SK - wk * BK;   // valid k within this group's columns
-                u32x4 bcur[FN][BH];
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FN; ++fn) {
+                const uint32_t w = breg[s][fn][ks >> 2][ks & 3];
+                bf[ks][fn][0] = (int)(w & 0x03030303u);
+                bf[ks][fn][1] = (int)((w >> 2) & 0x03030303u);
+                bf[ks][fn][2] = (int)((w >> 4) & 0x03030303u);
+                bf[ks][fn][3] = (int)((w >> 6) & 0x03030303u);
+            }
+        if (reload)
+            load(areg[s], breg[s], (it + P) * SK);
+        const uint8_t* Ab = As[buf];
+        v4i af[KS][FM];
 #pragma unroll
-                    for (int h = 0; h < BH; ++h) {
-                        bcur[fn][h] = breg[s][fn][h];
-                        if (128 * h + 64 * (lane >> 5) >= kvalid)
-                            bcur[fn][h] = u32x4{0u, 0u, 0u, 0u};
-                    }
-                if (it + P < nk)
-                    load(areg[s], breg[s], (it + P) * SK);
-                // All operands of the step first (one LDS round trip, unpack on the
-                // VALU), then the 4 * FM * FN matrix instructions back to back.
-                const uint8_t* Ab = As[buf];
-                v4i af[KS][FM];
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
+            for (int fm = 0; fm < FM; ++fm) {
+                const int r = wm * TM + fm * 32 + (lane & 31);
+                af[ks][fm] = *reinterpret_cast<const v4i*>(Ab + r * AST + wk * BK + 128 * (ks >> 2) +
+                                                           64 * (lane >> 5) + 16 * (ks & 3));
+            }
 #pragma unroll
-                    for (int fm = 0; fm < FM; ++fm) {
-                        const int r = wm * TM + fm * 32 + (lane & 31);
-                        af[ks][fm] = *reinterpret_cast<const v4i*>(Ab + r * AST + wk * BK + 128 * (ks >> 2) +
-                                                                   64 * (lane >> 5) + 16 * (ks & 3));
-                    }
-                v4i bf[KS][FN];
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
+            for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                    for (int fn = 0; fn < FN; ++fn) {
-                        const uint32_t w = bcur[fn][ks >> 2][ks & 3];
-                        bf[ks][fn][0] = (int)(w & 0x03030303u);
-                        bf[ks][fn][1] = (int)((w >> 2) & 0x03030303u);
-                        bf[ks][fn][2] = (int)((w >> 4) & 0x03030303u);
-                        bf[ks][fn][3] = (int)((w >> 6) & 0x03030303u);
-                    }
+                for (int fm = 0; fm < FM; ++fm)
+                    C[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][fm], bf[ks][fn], C[fm][fn], 0, 0, 0);
+        if constexpr (SCHED) {
+            // Interleave: each matrix instruction is followed by a few VALU (unpack) and
+            // LDS reads, so they issue while the MFMA executes.
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                        for (int fm = 0; fm < FM; ++fm)
-                            C[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][fm], bf[ks][fn], C[fm][fn], 0, 0, 0);
-                if constexpr (SCHED) {
-                    // Interleave: each matrix instruction is followed by a few VALU
-                    // (unpack) and LDS reads, so they issue while the MFMA executes.
-#pragma unroll
-                    for (int q = 0; q < KS * FM * FN; ++q) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, (7 * FN * 4 + 4 * FM * FN) / (4 * FM * FN) + 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    }
-                }
-                if (it + 1 < nk)
-                    store_a(areg[(s + 1) % P], buf ^ 1, K - (it + 1) * SK);
-                __syncthreads();
+            for (int q = 0; q < KS * FM * FN; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, (7 * FN * 4 + 4 * FM * FN) / (4 * FM * FN) + 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
         }
+        if (stage)
+            store_a(areg[(s + 1) % P], buf ^ 1, K - (it + 1) * SK, tail);
+        __syncthreads();
+    };
+
+    // Steady state: every step refills its slot and stages a step that lies wholly inside
+    // K, with no conditions, so the ring slots stay in fixed registers and a step waits
+    // only for its own loads (a conditional refill would make the compiler rotate the ring
+    // through register copies, which must wait for every load in flight).
+    int it = 0;
+    for (; it + 2 * P <= nk; it += P) {
+#pragma unroll
+        for (int s = 0; s < P; ++s)
+            step(it + s, s, true, true, false);
+    }
+    // The last (fewer than 2P) steps.
+#pragma unroll
+    for (int s = 0; s < 2 * P - 1; ++s) {
+        const int t = it + s;
+        if (t < nk)
+            step(t, s % P, t + P < nk, t + 1 < nk, true);
     }
 
     // Row sums of the activation codes: thread tid holds rows (tid + 256 i) / UPR for
