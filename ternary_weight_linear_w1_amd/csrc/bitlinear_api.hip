@@ -202,8 +202,10 @@ void launch_generic(const bl::FwdArgs& a, hipStream_t stream)
 template <int BM, int BN, int WM, int WN, int P, int BK, int WK = 1>
 void launch_gemm(const bl::FwdArgs& f, hipStream_t stream)
 {
-    bl::GemmArgs a{f.Xq, f.xscale, f.W, f.gamma, f.Y, f.acc, (int)f.M, (int)f.N, f.K, f.residual};
-    const int64_t tiles = ((f.M + BM - 1) / BM) * ((f.N + BN - 1) / BN);
+    const int64_t tiles_m = (f.M + BM - 1) / BM, tiles_n = (f.N + BN - 1) / BN;
+    bl::GemmArgs a{f.Xq, f.xscale, f.W, f.gamma, f.Y, f.acc, (int)f.M, (int)f.N, f.K, f.residual,
+                   bl::gemm_region_split(tiles_m, tiles_n, BM, BN, f.K)};
+    const int64_t tiles = tiles_m * tiles_n;
     hipLaunchKernelGGL((bl::gemm_mfma_kernel<BM, BN, WM, WN, P, false, BK, WK>), dim3((unsigned)tiles), dim3(256), 0,
                        stream, a);
 }
@@ -234,16 +236,15 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
     if (((a.M + 31) / 32) * ((a.N + 127) / 128) >= INT32_MAX)
         return false;
     // Tile shapes from timing the 2B prefill (M = 512, 2048) and 100B (M = 64) shapes: the
-    // 64 x 256 tile (K steps of 128) is faster per tile, but a launch that fills less than
-    // three quarters of its rounds of resident blocks loses to 32 x 128 tiles (K steps of
-    // 256): at M = 2048 on MI355X, QKV (480 tiles, 94% of 512 slots) and up (84%) take the
-    // big tile, O and down (320 tiles, 62%) the small one.
+    // 64 x 256 tile (K steps of 128) is faster per tile (at M = 2048 on MI355X on all four
+    // 2B shapes, 62-94% of its 512 resident slots filled), but a launch that fills less than
+    // half of its rounds of resident blocks loses to 32 x 128 tiles (K steps of 256).
     if (a.M >= 1024) {
         const int64_t tiles = ((a.M + 63) / 64) * ((a.N + 255) / 256);
         const int64_t slots = int64_t(cu_count()) *
                               resident_blocks(bl::gemm_mfma_kernel<64, 256, 1, 4, 2, false, 128>, g_occ_gemm_big);
         const int64_t rounds = (tiles + slots - 1) / slots;
-        if (4 * tiles >= 3 * rounds * slots) {
+        if (2 * tiles >= rounds * slots) {
             launch_gemm<64, 256, 1, 4, 2, 128>(a, stream);
             return true;
         }

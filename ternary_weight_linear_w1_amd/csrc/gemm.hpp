@@ -38,16 +38,63 @@ struct GemmArgs {
     int N;
     int K;
     int residual;         // 1: Y[m][n] = fl32(Y[m][n] + y[m][n])
+    int gm;               // tile-grid regions along M (1, 2, 4 or 8; 8 / gm along N)
 };
 
 // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous range of tiles
-// so that the tiles sharing weight columns (consecutive ids, m fastest) share its L2.
+// in an order where such a range is a rectangle of the tile grid, so that the activation
+// rows and weight columns it needs stay in that XCD's L2. The grid is cut into gm x
+// (8 / gm) regions (gm chosen on the host to minimise one region's operand bytes), listed
+// region by region, m fastest inside a region.
 __device__ __forceinline__ int xcd_tile(int bid, int ntiles)
 {
     constexpr int kXcd = 8;
     const int per = ntiles / kXcd, rem = ntiles % kXcd;
     const int x = bid % kXcd, i = bid / kXcd;
     return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}
+
+// Host side: the region split gm (of 1, 2, 4, 8 along M; 8 / gm along N) whose region
+// needs the fewest operand bytes (its activation rows plus its packed weight columns).
+inline int gemm_region_split(int64_t tiles_m, int64_t tiles_n, int BM, int BN, int64_t K)
+{
+    int best = 1;
+    int64_t best_bytes = -1;
+    for (int gm = 1; gm <= 8; gm *= 2) {
+        const int gn = 8 / gm;
+        if (gm > tiles_m || gn > tiles_n)
+            continue;
+        const int64_t bytes = (tiles_m + gm - 1) / gm * BM * K + (tiles_n + gn - 1) / gn * BN * (K / 4);
+        if (best_bytes < 0 || bytes < best_bytes) {
+            best = gm;
+            best_bytes = bytes;
+        }
+    }
+    return best;
+}
+
+__device__ __forceinline__ void region_tile(int idx, int tiles_m, int tiles_n, int gm, int& tm, int& tn)
+{
+    const int gn = 8 / gm;
+    const int sm = (tiles_m + gm - 1) / gm, sn = (tiles_n + gn - 1) / gn;
+    tm = 0;
+    tn = 0;
+    for (int rn = 0; rn < gn; ++rn) {
+        const int n0 = rn * sn, nn = min(sn, tiles_n - n0);
+        if (nn <= 0)
+            break;
+        for (int rm = 0; rm < gm; ++rm) {
+            const int m0 = rm * sm, mm = min(sm, tiles_m - m0);
+            if (mm <= 0)
+                break;
+            if (idx < mm * nn) {
+                tm = m0 + idx % mm;
+                tn = n0 + idx / mm;
+                return;
+            }
+            idx -= mm * nn;
+        }
+    }
 }
 
 // Raw buffer loads: 32-bit offsets from a per-tile base and hardware zero-fill beyond the
@@ -93,9 +140,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
 
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
-    const int m0 = (tile % tiles_m) * BM;
-    const int n0 = (tile / tiles_m) * BN;
+    int tm, tn;
+    region_tile(xcd_tile(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, a.gm, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
 
     if (tid < BM) {
         const int m = m0 + tid;
@@ -293,6 +341,31 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
 
     // C layout of a 32x32 tile: lane l, register r -> column l % 32,
     // row 8 (r / 4) + 4 (l / 32) + r % 4. Each row's offset and scale are read once.
+    //
+    // Common case (whole tile inside N, plain output, no int32 copy, 32-bit byte offsets):
+    // buffer stores with the row's byte offset computed once and the 32-column step as the
+    // instruction's immediate; rows past M fall outside the buffer and are dropped.
+    if (n0 + BN <= N && !a.residual && !a.acc && (int64_t)(M + BM) * N < (int64_t(1) << 29)) {
+        const __amdgpu_buffer_rsrc_t ry =
+            __builtin_amdgcn_make_buffer_rsrc((void*)a.Y, (short)0, M * N * 4, kBufferFlags);
+        const int col = n0 + wn * TN + (lane & 31);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * TM + fm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int32_t off = rsum[row];
+                const float c = csc[row];
+                const int voff = ((m0 + row) * N + col) * 4;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const float yv = (float)(C[fm][fn][r] - off) * c;
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, yv), ry, voff + 128 * fn, 0, 0);
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
