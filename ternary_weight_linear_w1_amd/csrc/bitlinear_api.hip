@@ -206,7 +206,7 @@ void launch_gemm(const bl::FwdArgs& f, hipStream_t stream)
     bl::GemmArgs a{f.Xq, f.xscale, f.W, f.gamma, f.Y, f.acc, (int)f.M, (int)f.N, f.K, f.residual,
                    bl::gemm_region_split(tiles_m, tiles_n, BM, BN, f.K)};
     const int64_t tiles = tiles_m * tiles_n;
-    hipLaunchKernelGGL((bl::gemm_mfma_kernel<BM, BN, WM, WN, P, false, BK, WK>), dim3((unsigned)tiles), dim3(256), 0,
+    hipLaunchKernelGGL((bl::gemm_mfma_kernel<BM, BN, WM, WN, P, BK, WK>), dim3((unsigned)tiles), dim3(256), 0,
                        stream, a);
 }
 
@@ -235,16 +235,17 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
         return false;
     if (((a.M + 31) / 32) * ((a.N + 127) / 128) >= INT32_MAX)
         return false;
-    // Tile shapes from timing the 2B prefill (M = 512, 2048) and 100B (M = 64) shapes: the
-    // 64 x 256 tile (K steps of 128) is faster per tile (at M = 2048 on MI355X on all four
-    // 2B shapes, 62-94% of its 512 resident slots filled), but a launch that fills less than
-    // half of its rounds of resident blocks loses to 32 x 128 tiles (K steps of 256).
-    if (a.M >= 1024) {
+    // Tile shapes from timing the 2B prefill (M = 512, 2048) and 100B (M = 64) shapes on
+    // MI355X: the 64 x 256 tile (K steps of 128) is faster per tile, and wins whenever it
+    // fills at least 40% of its rounds of resident blocks (all four 2B shapes at M = 2048,
+    // the up projection at M = 512); below that, 32 x 128 tiles (K steps of 256), split
+    // along K inside the block when even those are few.
+    if (a.M >= 512) {
         const int64_t tiles = ((a.M + 63) / 64) * ((a.N + 255) / 256);
         const int64_t slots = int64_t(cu_count()) *
-                              resident_blocks(bl::gemm_mfma_kernel<64, 256, 1, 4, 2, false, 128>, g_occ_gemm_big);
+                              resident_blocks(bl::gemm_mfma_kernel<64, 256, 1, 4, 2, 128>, g_occ_gemm_big);
         const int64_t rounds = (tiles + slots - 1) / slots;
-        if (2 * tiles >= rounds * slots) {
+        if (5 * tiles >= 2 * rounds * slots) {
             launch_gemm<64, 256, 1, 4, 2, 128>(a, stream);
             return true;
         }
@@ -253,7 +254,7 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
     // split N in two and K in two, so twice as many blocks cover the GPU.
     const int64_t tiles = ((a.M + 31) / 32) * ((a.N + 127) / 128);
     const int64_t slots = int64_t(cu_count()) *
-                          resident_blocks(bl::gemm_mfma_kernel<32, 128, 1, 4, 2, false, 256>, g_occ_gemm_small);
+                          resident_blocks(bl::gemm_mfma_kernel<32, 128, 1, 4, 2, 256>, g_occ_gemm_small);
     if (4 * tiles <= slots)
         launch_gemm<32, 64, 1, 2, 2, 256, 2>(a, stream);
     else

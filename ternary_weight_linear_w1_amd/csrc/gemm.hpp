@@ -110,7 +110,7 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
 // wave group g (of WM x WN waves) multiplies columns g*BK .. g*BK + BK - 1; the groups'
 // int32 partial sums are added through LDS before the epilogue (exact, fixed order).
 // This gives narrow tiles (and so more blocks) for few tokens and long rows.
-template <int BM, int BN, int WM, int WN, int P, bool SCHED = false, int BK = 128, int WK = 1>
+template <int BM, int BN, int WM, int WN, int P, int BK = 128, int WK = 1>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
 {
     static_assert(WM * WN * WK == 4, "four waves per block");
@@ -263,16 +263,6 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm)
                     C[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][fm], bf[ks][fn], C[fm][fn], 0, 0, 0);
-        if constexpr (SCHED) {
-            // Interleave: each matrix instruction is followed by a few VALU (unpack) and
-            // LDS reads, so they issue while the MFMA executes.
-#pragma unroll
-            for (int q = 0; q < KS * FM * FN; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, (7 * FN * 4 + 4 * FM * FN) / (4 * FM * FN) + 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        }
         if (stage)
             store_a(areg[(s + 1) % P], buf ^ 1, K - (it + 1) * SK, tail);
         __syncthreads();
