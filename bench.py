@@ -294,6 +294,10 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary configurations")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only the decode-attention cases (a short program for kernel traces)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the M = 2048 prefill products (a short program for counter passes)")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_CSV", "OUT"),
+                    help="matrix-core busy fraction per GEMM launch from a rocprofv3 --pmc pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -305,6 +309,9 @@ def main():
 
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, command=args.trace_command)
+        return 0
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
         return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_bytes, TRAFFIC_FILE)
@@ -329,6 +336,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.attention_only:
         print(json.dumps({"attention_decode": run_attention(torch, bl, dev)}))
+        return 0
+    if args.prefill_only:
+        print(json.dumps({"2B_prefill_M2048": run_prefill(torch, bl, datagen, dev, 2048)}))
         return 0
 
     # ---- the 2B layer at M = 1
@@ -492,18 +502,7 @@ def run_extra(torch, bl, datagen, dev, mats2b):
         log("extra 100B M=%d: %s" % (M, r))
     # ---- prefill on the 2B shapes (pre-quantized forward), int8 TOPS
     for M in (512, 2048):
-        r = {}
-        for i, (name, N, K, mode) in enumerate(LAYER_2B):
-            m = Mat(torch, bl, datagen, 4, i + 4 * (M > 512), name, N, K, mode, M, 2, dev)
-            m.x = datagen.heavy_channel_acts_torch(M, K, datagen.stream_id(4, 1, i, 1), dev)
-            m.prequant(bl)
-            a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), 2, 10)
-            ops = 2.0 * M * N * K
-            r[name] = {"us": round(a * 1e6, 1), "TOPS": round(ops / a / 1e12, 2),
-                       "frac_int8_peak": round(ops / a / 1e12 / INT8_PEAK_TOPS, 4)}
-            del m
-        res["2B_prefill_M%d" % M] = r
-        log("extra prefill M=%d: %s" % (M, r))
+        res["2B_prefill_M%d" % M] = run_prefill(torch, bl, datagen, dev, M)
     # ---- five codes per byte (1.6 bits per weight) against the 2-bit fields, pre-quantized
     res["trits5_vs_2bit"] = run_trits5(torch, bl, datagen, dev)
     torch.cuda.empty_cache()
@@ -529,6 +528,66 @@ def run_extra(torch, bl, datagen, dev, mats2b):
     del w, packed, ws
     torch.cuda.empty_cache()
     return res
+
+
+def run_prefill(torch, bl, datagen, dev, M):
+    """The pre-quantized product on the 2B shapes at M tokens (int8 MFMA GEMM): time per
+    launch (graph of 10, two weight copies) and int8 TOPS against the 5 POPS dense peak."""
+    r = {}
+    for i, (name, N, K, mode) in enumerate(LAYER_2B):
+        m = Mat(torch, bl, datagen, 4, i + 4 * (M > 512), name, N, K, mode, M, 2, dev)
+        m.x = datagen.heavy_channel_acts_torch(M, K, datagen.stream_id(4, 1, i, 1), dev)
+        m.prequant(bl)
+        a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), 2, 10)
+        ops = 2.0 * M * N * K
+        r[name] = {"us": round(a * 1e6, 1), "TOPS": round(ops / a / 1e12, 2),
+                   "frac_int8_peak": round(ops / a / 1e12 / INT8_PEAK_TOPS, 4)}
+        del m
+    log("extra prefill M=%d: %s" % (M, r))
+    return r
+
+
+def summarize_mfma(counter_csv, out):
+    """Matrix-core busy fraction of each GEMM launch shape from one rocprofv3 --pmc pass
+    over `bench.py --prefill-only`. SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of every
+    MFMA (32 per v_mfma_i32_32x32x32_i8) over the 1024 SIMDs; SQ_CYCLES sums the launch's
+    cycles over the 32 shader engines (8 XCDs x 4), so the launch spans SQ_CYCLES / 32
+    cycles and the fraction is BUSY / (1024 * SQ_CYCLES / 32)."""
+    import csv
+    import statistics
+    vals = {}
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            if "gemm_mfma" not in r["Kernel_Name"]:
+                continue
+            key = (r["Kernel_Name"].replace("void ", "").split("(")[0], int(r["Grid_Size"]) // 256)
+            d = vals.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    with open(out, "w") as f:
+        f.write("# int8 matrix-core busy fraction of the prefill GEMM (2B shapes, M = 2048)\n")
+        f.write("# commands (GPU box, repository root in $R):\n")
+        f.write("#   cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU_MFMA_I8 "
+                "SQ_INSTS_VALU SQ_CYCLES SQ_BUSY_CU_CYCLES SQ_LDS_BANK_CONFLICT SQ_WAIT_ANY -d $R/gpurun_out/pmc_mfma "
+                "-o mfma --output-format csv -- python3 $R/bench.py --prefill-only\n")
+        f.write("#   python3 bench.py --summarize-mfma <mfma_counter_collection.csv> <this file>\n")
+        f.write("# busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs * SQ_CYCLES / 32 shader engines); valu/mfma = "
+                "SQ_INSTS_VALU / SQ_INSTS_VALU_MFMA_I8 (the VALU count includes the MFMAs);\n")
+        f.write("# coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (VALU issued while the matrix core "
+                "runs); medians over the launches of each shape\n#\n")
+        f.write("# %-44s %6s %6s %8s %9s %8s %10s\n" % ("kernel", "WGs", "calls", "busy", "valu/mfma", "coexec",
+                                                     "bank_confl"))
+        for key in sorted(vals):
+            rows = [d for d in vals[key].values() if "SQ_VALU_MFMA_BUSY_CYCLES" in d and d.get("SQ_CYCLES")]
+            if not rows:
+                continue
+            busy = statistics.median(d["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * d["SQ_CYCLES"] / 32.0) for d in rows)
+            vpm = statistics.median(d["SQ_INSTS_VALU"] / max(d["SQ_INSTS_VALU_MFMA_I8"], 1.0) for d in rows)
+            co = statistics.median(d["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(d["SQ_VALU_MFMA_BUSY_CYCLES"], 1.0)
+                                   for d in rows)
+            bc = statistics.median(d.get("SQ_LDS_BANK_CONFLICT", 0.0) for d in rows)
+            f.write("  %-44s %6d %6d %7.1f%% %9.2f %7.1f%% %10.0f\n" % (key[0][:44], key[1], len(rows), 100 * busy, vpm,
+                                                                  100 * co, bc))
+    log("wrote %s" % out)
 
 
 def run_trits5(torch, bl, datagen, dev):
