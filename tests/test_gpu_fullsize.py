@@ -57,6 +57,8 @@ def check_matrix(cfg, idx, N, K, mode, M, fused, heavy=False, sampled=False):
     else:
         xq, s = bl.bitlinear_quantize_act(x, gain, EPS, relu2)
         y, acc = bl.bitlinear_forward(xq, s, packed, gamma, acc=True)
+        # without the int32 copy the product takes another store path: same output bits
+        assert torch.equal(bl.bitlinear_forward(xq, s, packed, gamma).view(torch.int32), y.view(torch.int32))
     torch.cuda.synchronize()
     wh = w.cpu().numpy()
     xh = x.cpu().numpy()

@@ -232,23 +232,29 @@ def test_forward_misaligned_views():
 # ------------------------------------------------------------------------------ MFMA path (M >= 16)
 
 GEMM_CASES = [
-    # (M, N, K): token and feature tails, K steps of 64 and 128, both block shapes
+    # (M, N, K): token and feature tails, K steps of 64 and 128, all block shapes; whole
+    # 64 x 256 and 32 x 128 tiles (the store epilogue without bounds checks) with K tails
     (16, 33, 64), (17, 129, 192), (64, 256, 2560), (100, 70, 6912), (255, 300, 128), (256, 384, 2560),
     (300, 257, 1024), (512, 128, 8192), (2048, 96, 2560), (40, 1000, 28672),
+    (512, 512, 2560), (1024, 768, 1024), (2048, 512, 192), (600, 1024, 64), (32, 1024, 6912),
 ]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES)
 def test_gemm_parity(M, N, K):
+    """Codes, accumulators and outputs bit-exact against the oracle; the call without the
+    int32 copy (a different store path) gives the same output bits."""
     w = latents(N, K, 7000 + N + K)
     x = make_acts(M, K, 8000 + M + K, heavy=True)
     packed, gamma = bl.bitlinear_pack_weights(up(w))
     xq, s = bl.bitlinear_quantize_act(up(x))
     y, acc = bl.bitlinear_forward(xq, s, packed, gamma, acc=True)
+    y_plain = bl.bitlinear_forward(xq, s, packed, gamma)
     o = oracle.bitlinear(x, w)
     assert np.array_equal(down(xq), o["xq"])
     assert np.array_equal(down(acc), o["acc"])
     assert np.array_equal(down(y).view(np.int32), o["y"].view(np.int32))
+    assert np.array_equal(down(y_plain).view(np.int32), o["y"].view(np.int32))
 
 
 # ------------------------------------------------------------------------------ residual forms
