@@ -57,8 +57,11 @@ LAYER_100B = [("qkv", 10240, 8192, "plain"), ("o", 8192, 8192, "norm"), ("up", 2
               ("down", 8192, 28672, "relu2norm")]
 
 DOMINANT = "down"
-KERNEL_SRC = ["ternary_weight_linear_w1_amd/csrc/gemv.hpp", "ternary_weight_linear_w1_amd/csrc/device_common.hpp",
-              "ternary_weight_linear_w1_amd/csrc/bitlinear_api.hip"]
+# What decides the measured GEMV's traffic: its kernel, the shared device helpers, and the
+# GEMV launch-shape section of the API file (from its "forward dispatch" banner to the MFMA
+# GEMM section), so edits elsewhere in the library do not invalidate the counter file.
+KERNEL_SRC = ["ternary_weight_linear_w1_amd/csrc/gemv.hpp", "ternary_weight_linear_w1_amd/csrc/device_common.hpp"]
+DISPATCH_SRC = ("ternary_weight_linear_w1_amd/csrc/bitlinear_api.hip", "forward dispatch", "Many tokens: int8 MFMA GEMM")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_down_2B_M1_traffic.txt")
 
 
@@ -67,6 +70,11 @@ def kernel_hash() -> str:
     for p in KERNEL_SRC:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
+    path, start, end = DISPATCH_SRC
+    with open(os.path.join(ROOT, path), "rb") as f:
+        text = f.read()
+    i = text.index(start.encode())
+    h.update(text[i:text.index(end.encode(), i)])
     return h.hexdigest()[:16]
 
 
