@@ -85,6 +85,11 @@ CASES = [
     (1, 2, 2, 70, [69]),                 # plain multi-head
     (1, 32, 2, 200, [150]),              # 16 per KV head: two blocks per KV head
     (1, 1, 1, 1, [0]),                   # capacity 1
+    # more blocks than two per compute unit: the rotate launch, then blocks that walk
+    # several 64-position sub-chunks with a running maximum
+    (1, 20, 5, 32768, [32767]),          # 2B heads, long context
+    (8, 20, 5, 4096, [4095, 4000, 3000, 2047, 1024, 700, 64, 5]),   # 8 sequences at mixed positions
+    (2, 64, 8, 4096, [4095, 2222]),      # 100B heads: 8 query heads per KV head split in two blocks
 ]
 
 
