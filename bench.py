@@ -463,8 +463,60 @@ def main():
     return 0
 
 
+def run_cfg1(torch, bl, datagen, dev):
+    """One BitLinear, M = 1, K = N = 2560, latents N(0, 0.02^2), plain absmax input
+    (fused call), rotating weight copies."""
+    N = K = 2560
+    C = n_copies(N * K // 4)
+    w = datagen.gaussian_weights_torch(N, K, datagen.stream_id(1, 0, 0, 0), dev)
+    packed, gamma = bl.bitlinear_pack_weights(w)
+    del w
+    copies = [packed] + [packed.clone() for _ in range(C - 1)]
+    x = datagen.outlier_acts_torch(1, K, datagen.stream_id(1, 0, 0, 1), dev)
+    y = torch.empty((1, N), dtype=torch.float32, device=dev)
+    t = time_kernel(torch, lambda c: bl.bitlinear_forward_f32(x, copies[c], gamma, y=y), C, 400)
+    b = layer_bytes(N, K, 1, "plain")
+    out = {"us": round(t * 1e6, 3), "GB/s": round(b / t / 1e9, 1), "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+           "algorithmic_bytes": b}
+    log("extra cfg1 single BitLinear: %s" % out)
+    return out
+
+
+def run_peaks(torch, dev):
+    """Achievable peaks on this GPU, for context next to the specs: a streaming read (torch
+    sum over 1 GiB of fp32), a streaming copy (1 GiB read + 1 GiB written), and the vendor
+    int8 GEMM (torch._int_mm, int8 x int8 -> int32, hipBLASLt on ROCm) on the 2B prefill
+    shapes at M = 2048 (dense int8 weights: 4x the bytes of the packed ternary ones)."""
+    out = {}
+    x = torch.ones((1 << 28,), dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    t = time_kernel(torch, lambda c: x.sum(), 1, 10)
+    out["stream_read_GB/s"] = round(x.numel() * 4 / t / 1e9, 1)
+    t = time_kernel(torch, lambda c: y.copy_(x), 1, 10)
+    out["stream_copy_GB/s (read + write)"] = round(2 * x.numel() * 4 / t / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    gemm = {}
+    try:
+        for name, N, K, _ in LAYER_2B:
+            M = 2048
+            a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+            b = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev).t()   # [K][N], column-major
+            t = time_kernel(torch, lambda c: torch._int_mm(a, b), 1, 10)
+            gemm[name] = {"us": round(t * 1e6, 1), "TOPS": round(2.0 * M * N * K / t / 1e12, 2)}
+            del a, b
+    except Exception as e:   # not every torch build has the int8 GEMM on this GPU
+        gemm = {"unavailable": str(e)[:200]}
+    out["torch_int_mm_M2048"] = gemm
+    log("extra measured peaks: %s" % out)
+    return out
+
+
 def run_extra(torch, bl, datagen, dev, mats2b):
     res = {}
+    res["cfg1_single_M1"] = run_cfg1(torch, bl, datagen, dev)
+    res["measured_peaks"] = run_peaks(torch, dev)
+    torch.cuda.empty_cache()
     # ---- 2B layer at M = 4, 8 (pre-quantized forward)
     for M in (4, 8):
         C = 16

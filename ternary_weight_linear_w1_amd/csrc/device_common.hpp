@@ -113,132 +113,170 @@ __device__ __forceinline__ double wave_sum_f64(double v)
 }
 
 // ------------------------------------------------------------------------------------
-// Per-token statistics of the (activation + gain) input, shared by the standalone
-// quantizer and the fused GEMV prologue so that both produce the same bits. Blocks of
-// 256 threads.
+// Per-token prologue: statistics and codes of the (activation + gain) input, shared by
+// the standalone quantizer and the fused GEMV prologues so that both produce the same
+// bits. Blocks of 256 threads.
 //
-//   m     = max_k |w_k|,  w_k = act_v(u_k, up_k) * gain_k   (order-free)
-//   sumsq = sum_k v_k^2 in binary64: thread t adds the float4 groups g = t, t+256, ...
-//           in increasing order (components in order); the 256 thread sums are combined
-//           by the fixed DPP/readlane tree of wave_sum_f64 per wave, then as
-//           (w0 + w1) + (w2 + w3) over the four waves. The order depends only on K.
-// The w values of the first KEEP groups of each thread (g = tid + 256 i, i < KEEP) are
-// returned in `wk` so the caller can quantize them without re-reading.
-// Must be called by all 256 threads of the block. `slot` (0 or 1) picks the LDS scratch;
-// consecutive calls alternate it, so no barrier is needed after the call (a slot is
-// written again only after every thread has passed the next call's barrier, which
-// follows its reads of the slot).
+// A unit is 16 consecutive elements of a row (four float4 groups); thread t owns units
+// t, t + 256, t + 512, ... . Rows are read through buffer loads whose range ends at the
+// row end, so groups past it read as zero: a zero input adds nothing to the maximum or
+// the sum of squares and gets code 0, and loops may run past the row without checks.
+//
+//   v_k   = x_k, max(x_k, 0)^2, or max(x_k, 0)^2 * up_k     (act 0, 1, 2)
+//   w_k   = v_k * gain_k (RMSNorm input) or v_k
+//   m     = max_k |w_k|                                       (order-free)
+//   sumsq = sum_k v_k^2 in binary64 (v_k^2 is exact there): each thread adds its units in
+//           increasing order, elements in order; the 256 thread sums are combined by the
+//           fixed DPP/readlane tree of wave_sum_f64 per wave, then as (w0 + w1) + (w2 + w3)
+//           over the four waves. The order depends only on K.
+//
+// The activation kind and the norm are template parameters of the arithmetic (no
+// per-element selects); with_mode() turns the runtime values into them once.
 // ------------------------------------------------------------------------------------
 struct RowStats {
     float m;
     double sumsq;
 };
 
-// Loads of the first KEEP float4 groups of each thread (g = tid + 256 q), issued early
-// so that they are not queued behind other loads; groups past the row give x = 0, g = 1.
-template <int KEEP>
-__device__ __forceinline__ void row_load(const float* __restrict__ u, int K, const float* __restrict__ gain,
-                                         const float* __restrict__ up, float4 (&xa)[KEEP], float4 (&gb)[KEEP])
+constexpr int kRowFlags = 0x00020000;  // buffer descriptor word 3 (gfx9)
+
+// Buffer ranges of one token: x (the gate half when gated), y = up (gated) or gain (norm),
+// z = gain when gated and normed. An operand that is not used has an empty range.
+struct RowRes {
+    __amdgpu_buffer_rsrc_t x, y, z;
+};
+
+__device__ __forceinline__ RowRes row_res(const float* X, int64_t tok, int K, int act, const float* gain)
 {
-    const int G = K >> 2;
-#pragma unroll
-    for (int q = 0; q < KEEP; ++q) {
-        const int g = (int)threadIdx.x + q * 256;
-        xa[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        gb[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-        if (g < G) {
-            xa[q] = reinterpret_cast<const float4*>(u)[g];
-            const float* second = up ? up : gain;
-            if (second)
-                gb[q] = reinterpret_cast<const float4*>(second)[g];
-        }
+    const float* x = X + tok * (act == 2 ? 2 * (int64_t)K : (int64_t)K);
+    const float* y = act == 2 ? x + K : gain;
+    const float* z = act == 2 ? gain : nullptr;
+    RowRes r;
+    r.x = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, 4 * K, kRowFlags);
+    r.y = __builtin_amdgcn_make_buffer_rsrc((void*)(y ? y : x), (short)0, y ? 4 * K : 0, kRowFlags);
+    r.z = __builtin_amdgcn_make_buffer_rsrc((void*)(z ? z : x), (short)0, z ? 4 * K : 0, kRowFlags);
+    return r;
+}
+
+struct UnitRaw {
+    float4 x[4], y[4], z[4];
+};
+
+__device__ __forceinline__ float4 load_f4(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float f4_get(const float4& v, int c)
+{
+    return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+
+template <int ACT, bool NORM>
+struct Mode {
+    static constexpr int kAct = ACT;
+    static constexpr bool kNorm = NORM;
+    static constexpr bool kY = ACT == 2 || NORM;     // up or gain in y
+    static constexpr bool kZ = ACT == 2 && NORM;     // gain in z
+};
+
+// f(Mode<act, norm>{}) for the runtime activation kind (0, 1, 2) and norm flag.
+template <typename F>
+__device__ __forceinline__ void with_mode(int act, bool norm, F&& f)
+{
+    if (act == 0) {
+        if (norm) f(Mode<0, true>{}); else f(Mode<0, false>{});
+    } else if (act == 1) {
+        if (norm) f(Mode<1, true>{}); else f(Mode<1, false>{});
+    } else {
+        if (norm) f(Mode<2, true>{}); else f(Mode<2, false>{});
     }
 }
 
-// Statistics from values preloaded by row_load (KEEP > 0) or read here. WIDE keeps eight
-// loads per thread in flight over the groups it reads itself (for long rows in the
-// standalone quantizer; the summation order is unchanged, only registers grow).
-template <int KEEP, bool WIDE = false>
-__device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const float* __restrict__ gain, int act,
-                                  bool want_sumsq, const float* __restrict__ up,
-                                  const float4 (&xa)[KEEP > 0 ? KEEP : 1], const float4 (&gb)[KEEP > 0 ? KEEP : 1],
-                                  float4* wk, int slot)
+// Loads of unit u (elements 16u .. 16u + 15).
+template <class MD>
+__device__ __forceinline__ void unit_load(const RowRes& rr, int u, UnitRaw& in)
 {
-    const int tid = threadIdx.x;
-    const int G = K >> 2;
-    double s = 0.0;
-    float mx = 0.0f;
-    auto visit = [&](float4 a, float4 gv, float4 uv) -> float4 {
-        const float va[4] = {a.x, a.y, a.z, a.w};
-        const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
-        const float ub[4] = {uv.x, uv.y, uv.z, uv.w};
-        float wa[4];
+    const int off = u << 6;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float v = act_v(va[c], ub[c], act);
-            if (want_sumsq)
-                s += (double)v * (double)v;
-            wa[c] = gain ? v * ga[c] : v;
-            mx = fmaxf(mx, fabsf(wa[c]));
-        }
-        return make_float4(wa[0], wa[1], wa[2], wa[3]);
-    };
-    int g = tid;
-    if constexpr (KEEP > 0) {
-#pragma unroll
-        for (int q = 0; q < KEEP; ++q) {
-            if (g + q * 256 < G) {
-                // gb holds the up values when gated (the gain, a small shared vector, is
-                // then read here), else the gain
-                float4 gv = gb[q];
-                float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-                if (up) {
-                    uv = gb[q];
-                    gv = gain ? reinterpret_cast<const float4*>(gain)[g + q * 256]
-                              : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-                }
-                wk[q] = visit(xa[q], gv, uv);
-            }
-        }
-        g += KEEP * 256;
+    for (int q = 0; q < 4; ++q) {
+        in.x[q] = load_f4(rr.x, off + 16 * q);
+        if constexpr (MD::kY)
+            in.y[q] = load_f4(rr.y, off + 16 * q);
+        if constexpr (MD::kZ)
+            in.z[q] = load_f4(rr.z, off + 16 * q);
     }
-    // groups past the kept ones (WIDE: eight loads in flight per thread, visited in order,
-    // which is the same summation order as one group at a time)
-    for (; WIDE && g + 7 * 256 < G; g += 8 * 256) {
-        float4 a[8], gv[8], uv[8];
+}
+
+// x and y with y chosen at run time (a uniform branch), for loads that are issued before
+// the mode-specialised code is entered; z (gated and normed) is left to unit_load_z.
+__device__ __forceinline__ void unit_load_xy(const RowRes& rr, int u, bool ly, UnitRaw& in)
+{
+    const int off = u << 6;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            a[q] = reinterpret_cast<const float4*>(u)[g + q * 256];
-            gv[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-            uv[q] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-            if (gain)
-                gv[q] = reinterpret_cast<const float4*>(gain)[g + q * 256];
-            if (up)
-                uv[q] = reinterpret_cast<const float4*>(up)[g + q * 256];
+    for (int q = 0; q < 4; ++q)
+        in.x[q] = load_f4(rr.x, off + 16 * q);
+    if (ly) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            in.y[q] = load_f4(rr.y, off + 16 * q);
+    }
+}
+
+__device__ __forceinline__ void unit_load_z(const RowRes& rr, int u, float4 (&z)[4])
+{
+    const int off = u << 6;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        z[q] = load_f4(rr.z, off + 16 * q);
+}
+
+// w of the 16 elements of a unit, folded into the running max |w| and sum of v^2.
+template <class MD>
+__device__ __forceinline__ void unit_visit(const float4 (&x)[4], const float4 (&y)[4], const float4 (&z)[4],
+                                           float (&w)[16], float& mx, double& ss)
+{
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        float v = f4_get(x[e >> 2], e & 3);
+        if constexpr (MD::kAct >= 1) {
+            const float p = v > 0.0f ? v : 0.0f;
+            v = p * p;
         }
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            visit(a[q], gv[q], uv[q]);
+        if constexpr (MD::kAct == 2)
+            v = v * f4_get(y[e >> 2], e & 3);
+        float wv = v;
+        if constexpr (MD::kNorm) {
+            ss = __builtin_fma((double)v, (double)v, ss);   // = ss + v*v: the product is exact
+            wv = v * f4_get((MD::kAct == 2 ? z : y)[e >> 2], e & 3);
+        }
+        w[e] = wv;
+        mx = fmaxf(mx, fabsf(wv));
     }
-    for (; g < G; g += 256) {
-        const float4 a = reinterpret_cast<const float4*>(u)[g];
-        float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-        float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-        if (gain)
-            gv = reinterpret_cast<const float4*>(gain)[g];
-        if (up)
-            uv = reinterpret_cast<const float4*>(up)[g];
-        visit(a, gv, uv);
-    }
+}
+
+template <class MD>
+__device__ __forceinline__ void unit_visit(const UnitRaw& in, float (&w)[16], float& mx, double& ss)
+{
+    unit_visit<MD>(in.x, in.y, in.z, w, mx, ss);
+}
+
+// Block maximum and binary64 sum (fixed tree). Must be called by all 256 threads. `slot`
+// (0 or 1) picks the LDS scratch; consecutive calls alternate it, so no barrier is needed
+// after the call (a slot is written again only after every thread has passed the next
+// call's barrier, which follows its reads of the slot).
+__device__ __forceinline__ RowStats block_stats(float mx, double ss, bool want_sumsq, int slot)
+{
     __shared__ float redm[2][4];
     __shared__ double red[2][4];
+    const int tid = threadIdx.x;
     const int wv = tid / kWave;
     mx = wave_max(mx);
     if (want_sumsq)
-        s = wave_sum_f64(s);
+        ss = wave_sum_f64(ss);
     if ((tid & (kWave - 1)) == 0) {
         redm[slot][wv] = mx;
-        red[slot][wv] = s;
+        red[slot][wv] = ss;
     }
     __syncthreads();
     const float m = fmaxf(fmaxf(redm[slot][0], redm[slot][1]), fmaxf(redm[slot][2], redm[slot][3]));
@@ -248,14 +286,65 @@ __device__ RowStats row_stats_pre(const float* __restrict__ u, int K, const floa
     return RowStats{m, total};
 }
 
-template <int KEEP = 0, bool WIDE = false>
-__device__ RowStats row_stats(const float* __restrict__ u, int K, const float* __restrict__ gain, int act,
-                              bool want_sumsq, const float* __restrict__ up, int slot, float4* wk = nullptr)
+// Statistics of a whole row: units t, t + 256, ... read two at a time (the per-thread
+// order of the sum is unchanged).
+template <class MD>
+__device__ __forceinline__ RowStats row_stats_units(const RowRes& rr, int nunits, int slot)
 {
-    float4 xa[KEEP > 0 ? KEEP : 1], gb[KEEP > 0 ? KEEP : 1];
-    if constexpr (KEEP > 0)
-        row_load<KEEP>(u, K, gain, up, xa, gb);
-    return row_stats_pre<KEEP, WIDE>(u, K, gain, act, want_sumsq, up, xa, gb, wk, slot);
+    float mx = 0.0f;
+    double ss = 0.0;
+    for (int u = threadIdx.x; u < nunits; u += 512) {
+        UnitRaw a, b;
+        unit_load<MD>(rr, u, a);
+        unit_load<MD>(rr, u + 256, b);   // past the row: zeros, no effect
+        float w[16];
+        unit_visit<MD>(a, w, mx, ss);
+        unit_visit<MD>(b, w, mx, ss);
+    }
+    return block_stats(mx, ss, MD::kNorm, slot);
+}
+
+// Four int32 values (their low bytes) as the bytes 0..3 of a dword.
+__device__ __forceinline__ uint32_t pack_bytes(int c0, int c1, int c2, int c3)
+{
+    return __builtin_amdgcn_perm((uint32_t)c1, (uint32_t)c0, 0x0c0c0400u) |
+           __builtin_amdgcn_perm((uint32_t)c3, (uint32_t)c2, 0x04000c0cu);
+}
+
+// Codes round_half_even(w * sp) of a unit. sp = 127 / m' with m' >= max |w| over the row,
+// so |w * sp| <= 127 (1 + 2^-24)^2 < 127.5 and the clip to [-128, 127] can never act.
+// Natural order: dword q holds codes 4q .. 4q + 3 (bytes in order).
+__device__ __forceinline__ uint4 unit_codes(const float (&w)[16], float sp)
+{
+    int c[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        c[e] = (int)__builtin_rintf(w[e] * sp);
+    return make_uint4(pack_bytes(c[0], c[1], c[2], c[3]), pack_bytes(c[4], c[5], c[6], c[7]),
+                      pack_bytes(c[8], c[9], c[10], c[11]), pack_bytes(c[12], c[13], c[14], c[15]));
+}
+
+// Transposed order: dword f holds codes f, 4 + f, 8 + f, 12 + f, the order in which the
+// GEMV unpacks a dword of packed weights (field f of its four bytes).
+__device__ __forceinline__ uint4 unit_codes_t(const float (&w)[16], float sp)
+{
+    int c[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        c[e] = (int)__builtin_rintf(w[e] * sp);
+    return make_uint4(pack_bytes(c[0], c[4], c[8], c[12]), pack_bytes(c[1], c[5], c[9], c[13]),
+                      pack_bytes(c[2], c[6], c[10], c[14]), pack_bytes(c[3], c[7], c[11], c[15]));
+}
+
+// Sum over the 64 lanes of a wave (integer: exact in any order); every lane gets it.
+__device__ __forceinline__ int wave_sum_i32(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
 __device__ __forceinline__ void token_scales(const RowStats& st, int K, bool norm, float eps, float& sp, float& s)

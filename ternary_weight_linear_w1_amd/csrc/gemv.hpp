@@ -45,69 +45,59 @@ struct FwdArgs {
 constexpr int kBufFlags = 0x00020000;  // buffer descriptor word 3 (gfx9)
 constexpr int kOob = 0x7ffffff0;       // an offset past every buffer: loads give 0, stores drop
 
-// Codes of float4 group g (elements 4g..4g+3) as one little-endian dword (natural order).
-__device__ __forceinline__ uint32_t group_codes(float4 w, float sp)
-{
-    return (uint32_t)(act_code(w.x, sp) & 0xff) | ((uint32_t)(act_code(w.y, sp) & 0xff) << 8) |
-           ((uint32_t)(act_code(w.z, sp) & 0xff) << 16) | ((uint32_t)(act_code(w.w, sp) & 0xff) << 24);
-}
-
-// float4 groups per thread kept in VGPRs by the fused prologue: enough for the longest
-// row a tile shape serves (L * CPL chunks of 16 groups over 256 threads), at most 8.
-// Kernels start with cold instruction caches, so the unrolled prologue is kept no
-// longer than the row needs.
-template <int L, int CPL>
-constexpr int keep_groups()
-{
-    return (L * CPL + 15) / 16 < 8 ? (L * CPL + 15) / 16 : 8;
-}
-
-// Early loads of token 0 of a tile: the fp32 row (fused) or the int8 codes, issued
-// before the weight loads so that they are not queued behind them.
-constexpr int kPreUnits = 2;  // 16-byte int8 units per thread preloaded (K <= 8192)
-template <int KP, int MT>
-struct Pre {
-    float4 xa[KP];
-    float4 gb[KP];         // gain, or the up values when gated
-    uint4 q[kPreUnits];
-    float xs[MT];          // per-token scales of the tile (unfused)
-};
-
 __device__ __forceinline__ int64_t x_stride(const FwdArgs& a)
 {
     return a.act == 2 ? 2 * (int64_t)a.K : (int64_t)a.K;
 }
 
-template <bool FUSED, bool STAGE, int KP, int MT>
-__device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre<KP, MT>& p)
+// Units of 16 elements per thread whose w values the fused prologue keeps in registers
+// between its statistics and its codes: enough for the longest row a tile shape serves
+// (L * CPL chunks of four units over 256 threads), at most 2 with one row per lane and
+// one token per tile, else 1 (more weight or code registers would otherwise leave room for
+// one wave per SIMD). Further units are read again for their codes.
+template <int L, int MT, int CPL, int R>
+constexpr int kept_units()
 {
-    if constexpr (FUSED) {
-        const float* x = a.X + tok * x_stride(a);
-        row_load<KP>(x, a.K, a.gain, a.act == 2 ? x + a.K : nullptr, p.xa, p.gb);
-    } else {
-        if constexpr (STAGE) {
-            const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
-            const int units = a.K >> 4;
-#pragma unroll
-            for (int i = 0; i < kPreUnits; ++i) {
-                const int u = (int)threadIdx.x + 256 * i;
-                p.q[i] = u < units ? src[u] : make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-        // scales through vector loads (tokens past M read 0), so that no scalar-load
-        // wait sits in front of the weight loads
-        const int64_t left = a.M - tok;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(a.xscale + tok), (short)0, (int)(4 * (left < MT ? left : MT)), kBufFlags);
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-            p.xs[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * t, 0, 0));
-    }
+    constexpr int need = (L * CPL * 4 + 255) / 256, cap = R == 1 && MT == 1 ? 2 : 1;
+    return need < cap ? need : cap;
 }
 
-template <int MT, bool FUSED, int KP>
+// Early loads of token 0 of a tile for the pre-quantized product: the int8 codes and the
+// scales, issued before the weight loads so that they are not queued behind them.
+constexpr int kPreUnits = 2;  // 16-byte int8 units per thread preloaded (K <= 8192)
+template <int MT>
+struct Pre {
+    uint4 q[kPreUnits];
+    float xs[MT];          // per-token scales of the tile
+};
+
+template <bool STAGE, int MT>
+__device__ __forceinline__ void stage_preload(const FwdArgs& a, int64_t tok, Pre<MT>& p)
+{
+    if constexpr (STAGE) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
+        const int units = a.K >> 4;
+#pragma unroll
+        for (int i = 0; i < kPreUnits; ++i) {
+            const int u = (int)threadIdx.x + 256 * i;
+            p.q[i] = u < units ? src[u] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    // scales through vector loads (tokens past M read 0), so that no scalar-load wait
+    // sits in front of the weight loads
+    const int64_t left = a.M - tok;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.xscale + tok), (short)0, (int)(4 * (left < MT ? left : MT)), kBufFlags);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        p.xs[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * t, 0, 0));
+}
+
+// Pre-quantized codes of the tile's tokens to LDS (natural order, K/16 slots per token;
+// tokens past M get zeros).
+template <int MT>
 __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt, uint4* __restrict__ lds,
-                                            float (&s)[MT], const Pre<KP, MT>& pre)
+                                            float (&s)[MT], const Pre<MT>& pre)
 {
     constexpr int NT = 256;
     const int tid = threadIdx.x;
@@ -121,60 +111,105 @@ __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt
                 dst[u] = make_uint4(0u, 0u, 0u, 0u);
             continue;
         }
-        const int64_t tok = t0 + t;
-        if constexpr (FUSED) {
-            const float* x = a.X + tok * x_stride(a);
-            const float* up = a.act == 2 ? x + a.K : nullptr;
-            const bool norm = a.gain != nullptr;
-            float4 wk[KP];
-            RowStats st;
-            if (t == 0) {
-                st = row_stats_pre<KP>(x, a.K, a.gain, a.act, norm, up, pre.xa, pre.gb, wk, 0);
+        s[t] = pre.xs[t];
+        const uint4* src = reinterpret_cast<const uint4*>(a.Xq + (t0 + t) * (int64_t)a.K);
+        int u = tid;
+        if (t == 0) {
+#pragma unroll
+            for (int i = 0; i < kPreUnits; ++i, u += NT)
+                if (u < units)
+                    dst[u] = pre.q[i];
+        }
+        for (; u < units; u += NT)
+            dst[u] = src[u];
+    }
+}
+
+// Fused prologue of the tile's tokens, specialised by mode MD: statistics, token scales
+// s, and the codes in LDS in the order the product consumes them (slot u holds unit u
+// transposed, K/16 slots per token), plus each wave's sum of the codes in csum (the row
+// sum of the codes is their total). Token 0's first UK units come preloaded in `pre`.
+template <int MT, int UK, class MD>
+__device__ __forceinline__ void fused_stage(const FwdArgs& a, int64_t t0, int mt, uint4* __restrict__ lds,
+                                            float (&s)[MT], int (&csum)[MT][4], const UnitRaw (&pre)[UK])
+{
+    constexpr int NT = 256;
+    const int tid = threadIdx.x;
+    const int units = a.K >> 4;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        s[t] = 1.0f;
+        uint4* dst = lds + (size_t)t * units;
+        if (t >= mt) {
+            for (int u = tid; u < units; u += NT)
+                dst[u] = make_uint4(0u, 0u, 0u, 0u);
+            if ((tid & (kWave - 1)) == 0)
+                csum[t][tid / kWave] = 0;
+            continue;
+        }
+        const RowRes rr = row_res(a.X, t0 + t, a.K, MD::kAct, a.gain);
+        float w[UK][16];
+        float mx = 0.0f;
+        double ss = 0.0;
+        if (t == 0) {
+            if constexpr (MD::kZ) {
+                // the gain of the gated input is read here (not preloaded: registers)
+                float4 z[UK][4];
+#pragma unroll
+                for (int i = 0; i < UK; ++i)
+                    unit_load_z(rr, tid + NT * i, z[i]);
+#pragma unroll
+                for (int i = 0; i < UK; ++i)
+                    unit_visit<MD>(pre[i].x, pre[i].y, z[i], w[i], mx, ss);
             } else {
-                st = row_stats<KP>(x, a.K, a.gain, a.act, norm, up, t & 1, wk);
-            }
-            float sp;
-            token_scales(st, a.K, norm, a.eps, sp, s[t]);
-            uint32_t* words = reinterpret_cast<uint32_t*>(dst);
-            const int G = a.K >> 2;
 #pragma unroll
-            for (int q = 0; q < KP; ++q) {
-                const int g = tid + q * NT;
-                if (g < G)
-                    words[g] = group_codes(wk[q], sp);
-            }
-            for (int g = tid + KP * NT; g < G; g += NT) {
-                const float4 xv = reinterpret_cast<const float4*>(x)[g];
-                float4 gv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-                float4 uv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-                if (norm)
-                    gv = reinterpret_cast<const float4*>(a.gain)[g];
-                if (up)
-                    uv = reinterpret_cast<const float4*>(up)[g];
-                const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
-                const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
-                const float ub[4] = {uv.x, uv.y, uv.z, uv.w};
-                float wa[4];
-#pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    const float v = act_v(xa[f], ub[f], a.act);
-                    wa[f] = norm ? v * ga[f] : v;
-                }
-                words[g] = group_codes(make_float4(wa[0], wa[1], wa[2], wa[3]), sp);
+                for (int i = 0; i < UK; ++i)
+                    unit_visit<MD>(pre[i], w[i], mx, ss);
             }
         } else {
-            s[t] = pre.xs[t];
-            const uint4* src = reinterpret_cast<const uint4*>(a.Xq + tok * (int64_t)a.K);
-            int u = tid;
-            if (t == 0) {
+            UnitRaw in[UK];
 #pragma unroll
-                for (int i = 0; i < kPreUnits; ++i, u += NT)
-                    if (u < units)
-                        dst[u] = pre.q[i];
-            }
-            for (; u < units; u += NT)
-                dst[u] = src[u];
+            for (int i = 0; i < UK; ++i)
+                unit_load<MD>(rr, tid + NT * i, in[i]);
+#pragma unroll
+            for (int i = 0; i < UK; ++i)
+                unit_visit<MD>(in[i], w[i], mx, ss);
         }
+#pragma unroll 1
+        for (int u = tid + NT * UK; u < units; u += NT) {
+            UnitRaw in;
+            unit_load<MD>(rr, u, in);
+            float tmp[16];
+            unit_visit<MD>(in, tmp, mx, ss);
+        }
+        const RowStats st = block_stats(mx, ss, MD::kNorm, t & 1);
+        float sp;
+        token_scales(st, a.K, MD::kNorm, a.eps, sp, s[t]);
+        int cs = 0;
+        auto put = [&](int u, const float (&wv)[16]) {
+            const uint4 c = unit_codes_t(wv, sp);
+            dst[u] = c;
+            cs = __builtin_amdgcn_sdot4((int)c.x, 0x01010101, cs, false);
+            cs = __builtin_amdgcn_sdot4((int)c.y, 0x01010101, cs, false);
+            cs = __builtin_amdgcn_sdot4((int)c.z, 0x01010101, cs, false);
+            cs = __builtin_amdgcn_sdot4((int)c.w, 0x01010101, cs, false);
+        };
+#pragma unroll
+        for (int i = 0; i < UK; ++i)
+            if (tid + NT * i < units)
+                put(tid + NT * i, w[i]);
+#pragma unroll 1
+        for (int u = tid + NT * UK; u < units; u += NT) {
+            UnitRaw in;
+            unit_load<MD>(rr, u, in);
+            float wv[16], m2 = 0.0f;
+            double s2 = 0.0;
+            unit_visit<MD>(in, wv, m2, s2);
+            put(u, wv);
+        }
+        cs = wave_sum_i32(cs);
+        if ((tid & (kWave - 1)) == 0)
+            csum[t][tid / kWave] = cs;
     }
 }
 
@@ -221,6 +256,7 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
     constexpr int WPR = L > 64 ? L / 64 : 1;
     extern __shared__ uint4 lds_codes[];
     __shared__ int32_t xred[RG][WPR][R][MT];
+    __shared__ int csum[MT][4];   // per-wave code sums of the fused prologue
     const int tid = threadIdx.x;
     const int j = tid % L;
     const int slot = tid / L;
@@ -279,8 +315,17 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
         // Activations of token 0 first, then the first two passes of weights, then the
         // prologue arithmetic while the weights are in flight.
         constexpr bool DIRECT = !FUSED && L >= 64;
-        Pre<keep_groups<L, CPL>(), MT> pre;
-        stage_preload<FUSED, !DIRECT>(a, t0, pre);
+        constexpr int UK = kept_units<L, MT, CPL, R>();
+        Pre<MT> pre;
+        UnitRaw pu[UK];
+        if constexpr (FUSED) {
+            const RowRes rr = row_res(a.X, t0, a.K, a.act, a.gain);
+#pragma unroll
+            for (int i = 0; i < UK; ++i)
+                unit_load_xy(rr, tid + NT * i, a.act == 2 || a.gain != nullptr, pu[i]);
+        } else {
+            stage_preload<!DIRECT>(a, t0, pre);
+        }
         uint32_t act[MT][CPL][16];
         if constexpr (DIRECT) {
             // tokens past M and chunks past K read as zero
@@ -319,10 +364,17 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
                 s[t] = t < mt ? pre.xs[t] : 1.0f;
         } else {
             __syncthreads();  // LDS of the previous tile is no longer read
-            stage_codes<MT, FUSED>(a, t0, mt, lds_codes, s, pre);
+            if constexpr (FUSED)
+                with_mode(a.act, a.gain != nullptr, [&](auto md) {
+                    fused_stage<MT, UK, decltype(md)>(a, t0, mt, lds_codes, s, csum, pu);
+                });
+            else
+                stage_codes<MT>(a, t0, mt, lds_codes, s, pre);
             __syncthreads();
         }
 
+        // Codes of the lane's chunks for every token, in the unpack order, and the part
+        // of sum_k x_k the lane removes from its offset-code sum.
         int32_t xs[MT];
         float csc[MT];
 #pragma unroll
@@ -332,25 +384,41 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = j + i * L;
+                if constexpr (FUSED) {
+                    // already transposed; chunks past the row meet zero weights, so any
+                    // in-range codes serve (the row sum comes from the prologue)
+                    const int cc = c < KC ? c : KC - 1;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                    if constexpr (DIRECT)
-                        v = make_uint4(act[t][i][4 * d + 0], act[t][i][4 * d + 1], act[t][i][4 * d + 2],
-                                       act[t][i][4 * d + 3]);
-                    else if (c < KC)
-                        v = src[4 * c + d];
-                    uint32_t o[4];
-                    transpose_bytes(v.x, v.y, v.z, v.w, o);
-                    act[t][i][4 * d + 0] = o[0];
-                    act[t][i][4 * d + 1] = o[1];
-                    act[t][i][4 * d + 2] = o[2];
-                    act[t][i][4 * d + 3] = o[3];
+                    for (int d = 0; d < 4; ++d) {
+                        const uint4 v = src[4 * cc + d];
+                        act[t][i][4 * d + 0] = v.x;
+                        act[t][i][4 * d + 1] = v.y;
+                        act[t][i][4 * d + 2] = v.z;
+                        act[t][i][4 * d + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                        if constexpr (DIRECT)
+                            v = make_uint4(act[t][i][4 * d + 0], act[t][i][4 * d + 1], act[t][i][4 * d + 2],
+                                           act[t][i][4 * d + 3]);
+                        else if (c < KC)
+                            v = src[4 * c + d];
+                        uint32_t o[4];
+                        transpose_bytes(v.x, v.y, v.z, v.w, o);
+                        act[t][i][4 * d + 0] = o[0];
+                        act[t][i][4 * d + 1] = o[1];
+                        act[t][i][4 * d + 2] = o[2];
+                        act[t][i][4 * d + 3] = o[3];
+                    }
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        sum = __builtin_amdgcn_sdot4((int)act[t][i][q], 0x01010101, sum, false);
                 }
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    sum = __builtin_amdgcn_sdot4((int)act[t][i][q], 0x01010101, sum, false);
             }
+            if constexpr (FUSED)
+                sum = j == 0 ? (csum[t][0] + csum[t][1]) + (csum[t][2] + csum[t][3]) : 0;
             xs[t] = sum;
             csc[t] = gamma / s[t];
         }
@@ -467,9 +535,12 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(FwdArgs a)
             sp[t] = 1.0f;
             if (t < mt) {
                 if constexpr (FUSED) {
-                    const float* x = a.X + (t0 + t) * x_stride(a);
-                    const RowStats st =
-                        row_stats(x, a.K, a.gain, a.act, norm, a.act == 2 ? x + a.K : nullptr, calls++ & 1);
+                    const RowRes rr = row_res(a.X, t0 + t, a.K, a.act, a.gain);
+                    const int slot = calls++ & 1;
+                    RowStats st;
+                    with_mode(a.act, norm, [&](auto md) {
+                        st = row_stats_units<decltype(md)>(rr, (a.K + 15) >> 4, slot);
+                    });
                     token_scales(st, a.K, norm, a.eps, sp[t], s);
                 } else {
                     s = a.xscale[t0 + t];
