@@ -139,21 +139,24 @@ bool dispatch_mt1(const bl::FwdArgs& a, hipStream_t stream)
     if (KC <= 128) {
         if (!big)
             launch_k64<32, 1, 4, 1, FUSED>(a, 1, stream);
-        else if constexpr (FUSED)
-            launch_k64<32, 1, 4, 2, FUSED>(a, 2, stream);
+        else if constexpr (FUSED)  // two blocks per CU from ~20 MB of packed weights (100B QKV, up)
+            launch_k64<32, 1, 4, 1, FUSED>(a, a.N * (int64_t)a.K >= (int64_t(72) << 20) ? 2 : 1, stream);
         else  // one row per lane and more blocks keep the HBM queue fuller on long matrices
             launch_k64<32, 1, 4, 1, FUSED>(a, a.N * (int64_t)a.K >= (int64_t(128) << 20) ? 3 : 2, stream);
         return true;
     }
-    if (KC <= 256) { launch_k64<64, 1, 4, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 256) {  // the fused prologue keeps the whole row in registers: one block per CU
+        launch_k64<64, 1, 4, 1, FUSED>(a, FUSED ? 1 : 2, stream);
+        return true;
+    }
     if (KC <= 512) {
         if constexpr (FUSED)
-            launch_k64<128, 1, 4, 2, FUSED>(a, 1, stream);
+            launch_k64<128, 1, 4, 1, FUSED>(a, 1, stream);
         else
             launch_k64<256, 1, 2, 2, FUSED>(a, 3, stream);  // codes straight to registers
         return true;
     }
-    if (KC <= 1024) { launch_k64<256, 1, 4, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 1024) { launch_k64<256, 1, 4, 1, FUSED>(a, FUSED ? 1 : 2, stream); return true; }
     return false;
 }
 

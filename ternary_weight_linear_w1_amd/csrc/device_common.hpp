@@ -286,20 +286,22 @@ __device__ __forceinline__ RowStats block_stats(float mx, double ss, bool want_s
     return RowStats{m, total};
 }
 
-// Statistics of a whole row: units t, t + 256, ... read two at a time (the per-thread
-// order of the sum is unchanged).
-template <class MD>
+// Statistics of a whole row: units t, t + 256, ... read NB at a time (the per-thread
+// order of the sum is unchanged; units past the row read zeros and change nothing).
+template <class MD, int NB = 2>
 __device__ __forceinline__ RowStats row_stats_units(const RowRes& rr, int nunits, int slot)
 {
     float mx = 0.0f;
     double ss = 0.0;
-    for (int u = threadIdx.x; u < nunits; u += 512) {
-        UnitRaw a, b;
-        unit_load<MD>(rr, u, a);
-        unit_load<MD>(rr, u + 256, b);   // past the row: zeros, no effect
+    for (int u = threadIdx.x; u < nunits; u += NB * 256) {
+        UnitRaw in[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            unit_load<MD>(rr, u + 256 * b, in[b]);
         float w[16];
-        unit_visit<MD>(a, w, mx, ss);
-        unit_visit<MD>(b, w, mx, ss);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            unit_visit<MD>(in[b], w, mx, ss);
     }
     return block_stats(mx, ss, MD::kNorm, slot);
 }

@@ -50,16 +50,35 @@ __device__ __forceinline__ int64_t x_stride(const FwdArgs& a)
     return a.act == 2 ? 2 * (int64_t)a.K : (int64_t)a.K;
 }
 
-// Units of 16 elements per thread whose w values the fused prologue keeps in registers
-// between its statistics and its codes: enough for the longest row a tile shape serves
-// (L * CPL chunks of four units over 256 threads), at most 2 with one row per lane and
-// one token per tile, else 1 (more weight or code registers would otherwise leave room for
-// one wave per SIMD). Further units are read again for their codes.
+// Units of 16 elements per thread in the fused prologue (thread t owns units t, t + 256,
+// ...): the longest row a tile shape serves has L * CPL chunks of four units.
+template <int L, int CPL>
+constexpr int units_per_thread()
+{
+    return (L * CPL * 4 + 255) / 256;
+}
+
+// Units per thread whose loads are issued before the weight loads (token 0): at most 2,
+// and 1 when the tile has more rows per lane or more tokens (their weight and code
+// registers would otherwise leave room for one wave per SIMD).
+template <int L, int MT, int CPL, int R>
+constexpr int preloaded_units()
+{
+    constexpr int need = units_per_thread<L, CPL>();
+    constexpr int cap = R == 1 && MT == 1 ? 2 : 1;
+    return need < cap ? need : cap;
+}
+
+// Units per thread whose w values stay in registers from the statistics to the codes:
+// up to 8 (128 registers) with one row per lane and one token per tile (with more than 2
+// these shapes take more than 256 registers and run one block per CU; a row of up to
+// 32768 elements is then read once), else the preloaded ones. Units past them are read
+// again for their codes.
 template <int L, int MT, int CPL, int R>
 constexpr int kept_units()
 {
-    constexpr int need = (L * CPL * 4 + 255) / 256, cap = R == 1 && MT == 1 ? 2 : 1;
-    return need < cap ? need : cap;
+    constexpr int need = units_per_thread<L, CPL>();
+    return R == 1 && MT == 1 ? (need < 8 ? need : 8) : preloaded_units<L, MT, CPL, R>();
 }
 
 // Early loads of token 0 of a tile for the pre-quantized product: the int8 codes and the
@@ -128,11 +147,14 @@ __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt
 // Fused prologue of the tile's tokens, specialised by mode MD: statistics, token scales
 // s, and the codes in LDS in the order the product consumes them (slot u holds unit u
 // transposed, K/16 slots per token), plus each wave's sum of the codes in csum (the row
-// sum of the codes is their total). Token 0's first UK units come preloaded in `pre`.
-template <int MT, int UK, class MD>
+// sum of the codes is their total). Token 0's first UP units come preloaded in `pre`;
+// the w values of the first NK units per thread stay in registers, further units are
+// read again for their codes.
+template <int MT, int UP, int NK, class MD>
 __device__ __forceinline__ void fused_stage(const FwdArgs& a, int64_t t0, int mt, uint4* __restrict__ lds,
-                                            float (&s)[MT], int (&csum)[MT][4], const UnitRaw (&pre)[UK])
+                                            float (&s)[MT], int (&csum)[MT][4], const UnitRaw (&pre)[UP])
 {
+    static_assert(UP >= 1 && NK >= UP, "kept units include the preloaded ones");
     constexpr int NT = 256;
     const int tid = threadIdx.x;
     const int units = a.K >> 4;
@@ -148,35 +170,48 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int64_t t0, int mt
             continue;
         }
         const RowRes rr = row_res(a.X, t0 + t, a.K, MD::kAct, a.gain);
-        float w[UK][16];
+        float w[NK][16];
         float mx = 0.0f;
         double ss = 0.0;
+        // first UP units (preloaded for token 0)
         if (t == 0) {
             if constexpr (MD::kZ) {
                 // the gain of the gated input is read here (not preloaded: registers)
-                float4 z[UK][4];
+                float4 z[UP][4];
 #pragma unroll
-                for (int i = 0; i < UK; ++i)
+                for (int i = 0; i < UP; ++i)
                     unit_load_z(rr, tid + NT * i, z[i]);
 #pragma unroll
-                for (int i = 0; i < UK; ++i)
+                for (int i = 0; i < UP; ++i)
                     unit_visit<MD>(pre[i].x, pre[i].y, z[i], w[i], mx, ss);
             } else {
 #pragma unroll
-                for (int i = 0; i < UK; ++i)
+                for (int i = 0; i < UP; ++i)
                     unit_visit<MD>(pre[i], w[i], mx, ss);
             }
         } else {
-            UnitRaw in[UK];
+            UnitRaw in[UP];
 #pragma unroll
-            for (int i = 0; i < UK; ++i)
+            for (int i = 0; i < UP; ++i)
                 unit_load<MD>(rr, tid + NT * i, in[i]);
 #pragma unroll
-            for (int i = 0; i < UK; ++i)
+            for (int i = 0; i < UP; ++i)
                 unit_visit<MD>(in[i], w[i], mx, ss);
         }
+        // further kept units, two loads in flight (units past the row read zeros)
+#pragma unroll
+        for (int i = UP; i < NK; i += 2) {
+            UnitRaw in0, in1;
+            unit_load<MD>(rr, tid + NT * i, in0);
+            if (i + 1 < NK)
+                unit_load<MD>(rr, tid + NT * (i + 1), in1);
+            unit_visit<MD>(in0, w[i], mx, ss);
+            if (i + 1 < NK)
+                unit_visit<MD>(in1, w[i + 1 < NK ? i + 1 : i], mx, ss);
+        }
+        // units past the kept ones (only tiles with several rows per lane or tokens)
 #pragma unroll 1
-        for (int u = tid + NT * UK; u < units; u += NT) {
+        for (int u = tid + NT * NK; u < units; u += NT) {
             UnitRaw in;
             unit_load<MD>(rr, u, in);
             float tmp[16];
@@ -195,11 +230,11 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int64_t t0, int mt
             cs = __builtin_amdgcn_sdot4((int)c.w, 0x01010101, cs, false);
         };
 #pragma unroll
-        for (int i = 0; i < UK; ++i)
+        for (int i = 0; i < NK; ++i)
             if (tid + NT * i < units)
                 put(tid + NT * i, w[i]);
 #pragma unroll 1
-        for (int u = tid + NT * UK; u < units; u += NT) {
+        for (int u = tid + NT * NK; u < units; u += NT) {
             UnitRaw in;
             unit_load<MD>(rr, u, in);
             float wv[16], m2 = 0.0f;
@@ -315,13 +350,14 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
         // Activations of token 0 first, then the first two passes of weights, then the
         // prologue arithmetic while the weights are in flight.
         constexpr bool DIRECT = !FUSED && L >= 64;
-        constexpr int UK = kept_units<L, MT, CPL, R>();
+        constexpr int UP = preloaded_units<L, MT, CPL, R>();
+        constexpr int NK = kept_units<L, MT, CPL, R>();
         Pre<MT> pre;
-        UnitRaw pu[UK];
+        UnitRaw pu[UP];
         if constexpr (FUSED) {
             const RowRes rr = row_res(a.X, t0, a.K, a.act, a.gain);
 #pragma unroll
-            for (int i = 0; i < UK; ++i)
+            for (int i = 0; i < UP; ++i)
                 unit_load_xy(rr, tid + NT * i, a.act == 2 || a.gain != nullptr, pu[i]);
         } else {
             stage_preload<!DIRECT>(a, t0, pre);
@@ -366,7 +402,7 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
             __syncthreads();  // LDS of the previous tile is no longer read
             if constexpr (FUSED)
                 with_mode(a.act, a.gain != nullptr, [&](auto md) {
-                    fused_stage<MT, UK, decltype(md)>(a, t0, mt, lds_codes, s, csum, pu);
+                    fused_stage<MT, UP, NK, decltype(md)>(a, t0, mt, lds_codes, s, csum, pu);
                 });
             else
                 stage_codes<MT>(a, t0, mt, lds_codes, s, pre);

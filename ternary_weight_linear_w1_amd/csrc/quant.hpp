@@ -23,9 +23,12 @@ struct QuantArgs {
     int act;             // 0 identity, 1 squared ReLU, 2 gated squared ReLU
 };
 
-// Pass 1: block statistics of the token. Pass 2: codes, sixteen per thread and step; the
-// row is read again (it is L2-resident after pass 1). Both passes visit the units in the
-// order of the fused GEMV prologue, so the two entry points give the same bits.
+// Pass 1: block statistics of the token. Pass 2: codes; the row is read again (it is
+// L2-resident after pass 1). Both passes keep kQuantUnits units of 16 elements per thread
+// in flight and visit the units in the order of the fused GEMV prologue, so the two entry
+// points give the same bits.
+constexpr int kQuantUnits = 4;
+
 __global__ __launch_bounds__(256) void quantize_act_kernel(QuantArgs a)
 {
     int calls = 0;  // statistics calls so far: their LDS slots alternate
@@ -33,9 +36,10 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(QuantArgs a)
     const bool wide = (a.K & 15) == 0;   // whole units: one 16-byte store each
     with_mode(a.act, a.gain != nullptr, [&](auto md) {
         using MD = decltype(md);
+        constexpr int NB = kQuantUnits;
         for (int64_t t = blockIdx.x; t < a.M; t += gridDim.x) {
             const RowRes rr = row_res(a.X, t, a.K, MD::kAct, a.gain);
-            const RowStats st = row_stats_units<MD>(rr, units, calls++ & 1);
+            const RowStats st = row_stats_units<MD, NB>(rr, units, calls++ & 1);
             float sp, s;
             token_scales(st, a.K, MD::kNorm, a.eps, sp, s);
             if (threadIdx.x == 0)
@@ -43,24 +47,26 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(QuantArgs a)
             // the store range ends at the row end: codes of groups past it are dropped
             const __amdgpu_buffer_rsrc_t out =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(a.Xq + t * (int64_t)a.K), (short)0, a.K, kRowFlags);
-            for (int u = threadIdx.x; u < units; u += 512) {
-                UnitRaw in0, in1;
-                unit_load<MD>(rr, u, in0);
-                unit_load<MD>(rr, u + 256, in1);
-                float w0[16], w1[16], m = 0.0f;
-                double q = 0.0;
-                unit_visit<MD>(in0, w0, m, q);
-                unit_visit<MD>(in1, w1, m, q);
-                const uint4 c0 = unit_codes(w0, sp), c1 = unit_codes(w1, sp);
-                if (wide) {
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, c0), out, 16 * u, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, c1), out, 16 * (u + 256), 0, 0);
-                } else {
-                    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            for (int u = threadIdx.x; u < units; u += NB * 256) {
+                UnitRaw in[NB];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        __builtin_amdgcn_raw_buffer_store_b32((int)cw[e], out, 16 * (u + 256 * (e >> 2)) + 4 * (e & 3),
-                                                              0, 0);
+                for (int b = 0; b < NB; ++b)
+                    unit_load<MD>(rr, u + 256 * b, in[b]);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    float w[16], m = 0.0f;
+                    double q = 0.0;
+                    unit_visit<MD>(in[b], w, m, q);
+                    const uint4 c = unit_codes(w, sp);
+                    const int ub = u + 256 * b;
+                    if (wide) {
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, c), out, 16 * ub, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b32((int)c.x, out, 16 * ub, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32((int)c.y, out, 16 * ub + 4, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32((int)c.z, out, 16 * ub + 8, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32((int)c.w, out, 16 * ub + 12, 0, 0);
+                    }
                 }
             }
         }
