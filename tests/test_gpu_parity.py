@@ -187,6 +187,10 @@ FWD_CASES = [
     (1, 2560, 2560, None),
     (1, 2560, 6912, "gatednorm"), (4, 70, 2560, "gatednorm"), (2, 33, 260, "gatednorm"),
     (1, 50, 28672, "gatednorm"), (3, 17, 128, "gated"), (8, 300, 6912, "gatednorm"),
+    # one-token tiles of the fused prologue: 4 and 8 units per thread kept in registers,
+    # rows past 8 units re-read for their codes, every activation kind with and without norm
+    (1, 33, 16384, "norm"), (1, 40, 65536, "relu2norm"), (1, 24, 65536, "gatednorm"), (1, 20, 65536, "gated"),
+    (1, 40, 28672, "gated"), (1, 50, 8192, "relu2"), (1, 30, 32768, "norm"),
 ]
 
 
