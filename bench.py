@@ -61,7 +61,8 @@ DOMINANT = "down"
 # GEMV launch-shape section of the API file (from its "forward dispatch" banner to the MFMA
 # GEMM section), so edits elsewhere in the library do not invalidate the counter file.
 KERNEL_SRC = ["ternary_weight_linear_w1_amd/csrc/gemv.hpp", "ternary_weight_linear_w1_amd/csrc/device_common.hpp"]
-DISPATCH_SRC = ("ternary_weight_linear_w1_amd/csrc/bitlinear_api.hip", "forward dispatch", "Many tokens: int8 MFMA GEMM")
+# the launch of one-token tiles (launch_k64 and the one-token dispatch) decides the measured kernel's grid
+DISPATCH_SRC = ("ternary_weight_linear_w1_amd/csrc/bitlinear_api.hip", "forward dispatch", "// Two tokens per tile")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_down_2B_M1_traffic.txt")
 
 
@@ -517,18 +518,24 @@ def run_extra(torch, bl, datagen, dev, mats2b):
     res["cfg1_single_M1"] = run_cfg1(torch, bl, datagen, dev)
     res["measured_peaks"] = run_peaks(torch, dev)
     torch.cuda.empty_cache()
-    # ---- 2B layer at M = 4, 8 (pre-quantized forward)
+    # ---- 2B layer at M = 4, 8: the fused call, the product on pre-quantized codes and the
+    # quantization launch on its own (weights rotating as at M = 1)
     for M in (4, 8):
-        C = 16
         r = {}
         for i, (name, N, K, mode) in enumerate(LAYER_2B):
+            C = n_copies(N * K // 4)
             m = Mat(torch, bl, datagen, 2, 8 + i, name, N, K, mode, M, C, dev)
+            f = time_kernel(torch, lambda c, m=m: m.fused(bl, c), C, 200)
             m.prequant(bl)
             a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), C, 200)
-            b = m.bytes(fused=False)
-            r[name] = {"us": round(a * 1e6, 3), "GB/s": round(b / a / 1e9, 1)}
+            q = time_kernel(torch, lambda c, m=m: m.prequant(bl), 1, 200)
+            b, fb = m.bytes(fused=False), m.bytes()
+            r[name] = {"fused_us": round(f * 1e6, 3), "fused_GB/s": round(fb / f / 1e9, 1),
+                       "forward_us": round(a * 1e6, 3), "forward_GB/s": round(b / a / 1e9, 1),
+                       "quantize_us": round(q * 1e6, 3)}
             del m
-        res["2B_M%d_forward" % M] = r
+            torch.cuda.empty_cache()
+        res["2B_M%d" % M] = r
         log("extra 2B M=%d: %s" % (M, r))
     torch.cuda.empty_cache()
     # ---- 100B-shaped slice at M = 1 (fused) and M = 64 (pre-quantized)

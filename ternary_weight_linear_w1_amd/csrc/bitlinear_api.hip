@@ -99,11 +99,14 @@ void launch_k64(const bl::FwdArgs& a, int wg_per_cu, hipStream_t stream)
     constexpr int RPP = (256 / L) * R;
     const int64_t passes = (a.N + RPP - 1) / RPP;
     const int64_t tiles = (a.M + MT - 1) / MT;
-    const int64_t max_x = int64_t(cu_count()) * wg_per_cu;
-    const int gx = (int)(passes < max_x ? passes : max_x);
     const int gy = (int)(tiles < 65535 ? tiles : 65535);
+    // fused multi-token tiles take one block per CU (their prologue holds more than 256
+    // registers), so the token tiles share the CUs instead of queueing for a second round
+    const int64_t max_x = FUSED && MT > 1 ? std::max<int64_t>(1, (int64_t(cu_count()) * wg_per_cu + gy - 1) / gy)
+                                          : int64_t(cu_count()) * wg_per_cu;
+    const int gx = (int)(passes < max_x ? passes : max_x);
     // pre-quantized codes with L >= 64 go straight to registers (no LDS staging)
-    const size_t lds = (!FUSED && L >= 64) ? 0 : (size_t)MT * (size_t)a.K;
+    const size_t lds = (!FUSED && L >= 64) ? 0 : FUSED ? bl::fused_lds_bytes<L, MT, CPL>(a.K) : (size_t)MT * a.K;
     if (a.residual) {
         // (the row loop strides by the grid, so any grid width is correct)
         if constexpr (MT * R <= 4)
@@ -173,20 +176,23 @@ bool dispatch_mt2(const bl::FwdArgs& a, hipStream_t stream)
     return false;
 }
 
-// Four tokens per tile: one chunk per lane.
+// Four tokens per tile: one chunk per lane. Blocks per CU from graph-timed sweeps of the 2B
+// shapes at 3, 4, 8 and 16 tokens: two with a single pre-quantized tile, one once there are
+// several tiles (they already give the grid two or more blocks per CU) or a fused prologue.
 template <bool FUSED>
 bool dispatch_mt4(const bl::FwdArgs& a, hipStream_t stream)
 {
     const int KC = a.K / 64;
     const bool big = a.N * (int64_t)a.K >= (int64_t(64) << 20);
-    if (KC <= 64) { launch_k64<64, 4, 1, 1, FUSED>(a, 2, stream); return true; }
+    const int wg = FUSED || a.M > 4 ? 1 : 2;
+    if (KC <= 64) { launch_k64<64, 4, 1, 1, FUSED>(a, wg, stream); return true; }
     if (KC <= 128) {
         // four rows per lane need the registers the residual loads take
-        if (big && !a.residual) launch_k64<128, 4, 1, 4, FUSED>(a, 2, stream);
-        else launch_k64<128, 4, 1, 1, FUSED>(a, 2, stream);
+        if (big && !a.residual) launch_k64<128, 4, 1, 4, FUSED>(a, wg, stream);
+        else launch_k64<128, 4, 1, 1, FUSED>(a, wg, stream);
         return true;
     }
-    if (KC <= 256) { launch_k64<256, 4, 1, 1, FUSED>(a, 2, stream); return true; }
+    if (KC <= 256) { launch_k64<256, 4, 1, 1, FUSED>(a, wg, stream); return true; }
     return false;
 }
 

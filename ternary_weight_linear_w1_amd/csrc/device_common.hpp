@@ -286,6 +286,48 @@ __device__ __forceinline__ RowStats block_stats(float mx, double ss, bool want_s
     return RowStats{m, total};
 }
 
+// block_stats for MT tokens at once (one barrier); each token's sum in the same order.
+// Its LDS scratch is rewritten only after the caller's next block-wide barrier.
+template <int MT>
+__device__ __forceinline__ void block_stats_multi(const float (&mx)[MT], const double (&ss)[MT], bool want_sumsq,
+                                                  RowStats (&st)[MT])
+{
+    __shared__ float redm[MT][4];
+    __shared__ double red[MT][4];
+    const int tid = threadIdx.x;
+    const int wv = tid / kWave;
+    float m[MT];
+    double q[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        m[t] = wave_max(mx[t]);
+        q[t] = want_sumsq ? wave_sum_f64(ss[t]) : 0.0;
+    }
+    if ((tid & (kWave - 1)) == 0) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            redm[t][wv] = m[t];
+            red[t][wv] = q[t];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        st[t].m = fmaxf(fmaxf(redm[t][0], redm[t][1]), fmaxf(redm[t][2], redm[t][3]));
+        st[t].sumsq = want_sumsq ? (red[t][0] + red[t][1]) + (red[t][2] + red[t][3]) : 0.0;
+    }
+}
+
+// Buffer ranges that read nothing (every load gives zeros).
+__device__ __forceinline__ RowRes row_res_empty(const float* any)
+{
+    RowRes r;
+    r.x = __builtin_amdgcn_make_buffer_rsrc((void*)any, (short)0, 0, kRowFlags);
+    r.y = r.x;
+    r.z = r.x;
+    return r;
+}
+
 // Statistics of a whole row: units t, t + 256, ... read NB at a time (the per-thread
 // order of the sum is unchanged; units past the row read zeros and change nothing).
 template <class MD, int NB = 2>

@@ -81,6 +81,28 @@ constexpr int kept_units()
     return R == 1 && MT == 1 ? (need < 8 ? need : 8) : preloaded_units<L, MT, CPL, R>();
 }
 
+// Multi-token tiles of the fused prologue stage the w values of units 1 .. NS per thread
+// in LDS (16 KB per unit index and token, after the codes), within a budget that leaves
+// room for the blocks per CU these tiles run with (one for four tokens, two for two);
+// units past them are read again for their codes.
+template <int L, int MT, int CPL>
+constexpr int staged_units()
+{
+    constexpr int need = units_per_thread<L, CPL>() - 1;
+    constexpr int budget = (MT >= 4 ? 150 : 78) * 1024 - MT * L * CPL * 64;
+    constexpr int fit = budget > 0 ? budget / (MT * 16384) : 0;
+    return MT == 1 ? 0 : (need < fit ? need : fit);
+}
+
+// Dynamic LDS bytes of a fused or staged launch: the codes, then the staged w values.
+template <int L, int MT, int CPL>
+constexpr size_t fused_lds_bytes(int K)
+{
+    const int nU = (K / 16 + 255) / 256;
+    const int ns = staged_units<L, MT, CPL>() < nU - 1 ? staged_units<L, MT, CPL>() : nU - 1;
+    return (size_t)MT * K + (size_t)(ns > 0 ? ns : 0) * MT * 16384;
+}
+
 // Early loads of token 0 of a tile for the pre-quantized product: the int8 codes and the
 // scales, issued before the weight loads so that they are not queued behind them.
 constexpr int kPreUnits = 2;  // 16-byte int8 units per thread preloaded (K <= 8192)
@@ -150,7 +172,7 @@ __device__ __forceinline__ void stage_codes(const FwdArgs& a, int64_t t0, int mt
 // sum of the codes is their total). Token 0's first UP units come preloaded in `pre`;
 // the w values of the first NK units per thread stay in registers, further units are
 // read again for their codes.
-template <int MT, int UP, int NK, class MD>
+template <int MT, int UP, int NK, int NS, class MD>
 __device__ __forceinline__ void fused_stage(const FwdArgs& a, int64_t t0, int mt, uint4* __restrict__ lds,
                                             float (&s)[MT], int (&csum)[MT][4], const UnitRaw (&pre)[UP])
 {
@@ -158,6 +180,132 @@ __device__ __forceinline__ void fused_stage(const FwdArgs& a, int64_t t0, int mt
     constexpr int NT = 256;
     const int tid = threadIdx.x;
     const int units = a.K >> 4;
+    if constexpr (MT > 1) {
+        // All tokens of the tile together, unit index by unit index: the gain is read once
+        // for every token, each token's w of unit 0 stays in registers, units 1 .. ns go to
+        // thread-private LDS slots and later ones are read again for their codes; one
+        // barrier reduces every token's statistics. Tokens past M read nothing (zero codes,
+        // dropped outputs).
+        static_assert(UP == 1, "multi-token tiles preload one unit of token 0");
+        RowRes rr[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            rr[t] = t < mt ? row_res(a.X, t0 + t, a.K, MD::kAct, a.gain) : row_res_empty(a.X);
+        const int nU = (units + NT - 1) / NT;
+        const int ns = NS < nU - 1 ? NS : nU - 1;
+        float4* stage = reinterpret_cast<float4*>(lds + (size_t)MT * units);
+        float w0[MT][16];
+        float mx[MT];
+        double ss[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            mx[t] = 0.0f;
+            ss[t] = 0.0;
+        }
+        // unit i of every token: loads (token 0's unit 0 preloaded), then visit(t, w)
+        auto unit = [&](int i, auto&& visit) {
+            const int off = (tid + NT * i) << 6;
+            float4 g[4], xs[MT][4], ups[MT][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (MD::kNorm) {
+                    if constexpr (MD::kAct == 2)
+                        g[q] = load_f4(rr[0].z, off + 16 * q);
+                    else
+                        g[q] = i == 0 ? pre[0].y[q] : load_f4(rr[0].y, off + 16 * q);
+                }
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    xs[t][q] = i == 0 && t == 0 ? pre[0].x[q] : load_f4(rr[t].x, off + 16 * q);
+                    if constexpr (MD::kAct == 2)
+                        ups[t][q] = i == 0 && t == 0 ? pre[0].y[q] : load_f4(rr[t].y, off + 16 * q);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                float wv[16];
+                if constexpr (MD::kAct == 2)
+                    unit_visit<MD>(xs[t], ups[t], g, wv, mx[t], ss[t]);
+                else
+                    unit_visit<MD>(xs[t], g, g, wv, mx[t], ss[t]);
+                visit(t, wv);
+            }
+        };
+        unit(0, [&](int t, const float (&wv)[16]) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                w0[t][e] = wv[e];
+        });
+#pragma unroll 1
+        for (int i = 1; i < nU; ++i)
+            unit(i, [&](int t, const float (&wv)[16]) {
+                if (i <= ns) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        stage[(((i - 1) * MT + t) * 4 + q) * NT + tid] =
+                            make_float4(wv[4 * q], wv[4 * q + 1], wv[4 * q + 2], wv[4 * q + 3]);
+                }
+            });
+        RowStats st[MT];
+        block_stats_multi<MT>(mx, ss, MD::kNorm, st);
+        float sp[MT];
+        int cs[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            float sv;
+            token_scales(st[t], a.K, MD::kNorm, a.eps, sp[t], sv);
+            s[t] = t < mt ? sv : 1.0f;
+            cs[t] = 0;
+        }
+        auto put = [&](int t, int u, const float (&wv)[16]) {
+            const uint4 c = unit_codes_t(wv, sp[t]);
+            lds[(size_t)t * units + u] = c;
+            cs[t] = __builtin_amdgcn_sdot4((int)c.x, 0x01010101, cs[t], false);
+            cs[t] = __builtin_amdgcn_sdot4((int)c.y, 0x01010101, cs[t], false);
+            cs[t] = __builtin_amdgcn_sdot4((int)c.z, 0x01010101, cs[t], false);
+            cs[t] = __builtin_amdgcn_sdot4((int)c.w, 0x01010101, cs[t], false);
+        };
+        if (tid < units) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                put(t, tid, w0[t]);
+        }
+#pragma unroll 1
+        for (int i = 1; i <= ns; ++i) {
+            const int u = tid + NT * i;
+            if (u < units) {
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    float wv[16];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 v = stage[(((i - 1) * MT + t) * 4 + q) * NT + tid];
+                        wv[4 * q] = v.x;
+                        wv[4 * q + 1] = v.y;
+                        wv[4 * q + 2] = v.z;
+                        wv[4 * q + 3] = v.w;
+                    }
+                    put(t, u, wv);
+                }
+            }
+        }
+        // units past the staged ones: statistics are done, read them again for the codes
+#pragma unroll 1
+        for (int i = ns + 1; i < nU; ++i) {
+            const int u = tid + NT * i;
+            unit(i, [&](int t, const float (&wv)[16]) {
+                if (u < units)
+                    put(t, u, wv);
+            });
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const int v = wave_sum_i32(cs[t]);
+            if ((tid & (kWave - 1)) == 0)
+                csum[t][tid / kWave] = v;
+        }
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         s[t] = 1.0f;
@@ -402,7 +550,8 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
             __syncthreads();  // LDS of the previous tile is no longer read
             if constexpr (FUSED)
                 with_mode(a.act, a.gain != nullptr, [&](auto md) {
-                    fused_stage<MT, UP, NK, decltype(md)>(a, t0, mt, lds_codes, s, csum, pu);
+                    fused_stage<MT, UP, NK, staged_units<L, MT, CPL>(), decltype(md)>(a, t0, mt, lds_codes, s,
+                                                                                      csum, pu);
                 });
             else
                 stage_codes<MT>(a, t0, mt, lds_codes, s, pre);
