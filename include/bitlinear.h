@@ -151,6 +151,32 @@ int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const f
                                    float* Y, hipStream_t stream);
 
 /*
+ * The fused call for any number of tokens, with a caller workspace (the same operation
+ * and result as bitlinear_forward_f32, or its residual form when residual != 0).
+ *
+ * One launch converts the input inside the product only while the tokens fit a few
+ * token tiles of the decode product; from 16 tokens on, every tile would read all the
+ * weights again. This entry then quantizes into the workspace and runs the matrix-core
+ * product: bit for bit bitlinear_quantize_act followed by bitlinear_forward (or
+ * bitlinear_forward_residual), the same result the one-launch call gives.
+ *
+ *   workspace        device scratch of at least bitlinear_forward_f32_workspace_bytes(M, K)
+ *                    bytes, 16-byte aligned, overlapping no argument; its contents after
+ *                    the call are unspecified; calls that may run concurrently need
+ *                    distinct workspaces. When that size is 0 (M < 16, or sizes out of
+ *                    range) the workspace is not used and may be NULL.
+ *   residual         0: Y = product; 1: Y = fl32(Y + product)
+ * Other arguments, layouts and errors as in bitlinear_forward_f32; additionally
+ * BITLINEAR_ERR_NULL for a NULL workspace and BITLINEAR_ERR_WORKSPACE for a short one
+ * when one is needed. bitlinear_forward_f32_workspace_bytes returns 0 for sizes out of
+ * range.
+ */
+size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t K);
+int bitlinear_forward_f32_ws(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
+                             const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int residual,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Five ternary codes per byte (1.6 bits per weight) instead of four: "微软AI大模型炸场"
  * s.3 packs several trits into one 8-bit integer, and "BitNet b1.58 深度解析" s.2.1 notes
  * that a 2-bit field leaves one of its four states unused; 3^5 = 243 <= 256.

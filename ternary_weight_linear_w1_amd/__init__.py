@@ -17,7 +17,8 @@ from ._build import LIB as _LIB_PATH
 
 __all__ = [
     "BitLinearError", "lib", "status_string", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
-    "bitlinear_quantize_act", "bitlinear_forward", "bitlinear_forward_f32", "bitlinear_attention_workspace_bytes",
+    "bitlinear_quantize_act", "bitlinear_forward", "bitlinear_forward_f32", "bitlinear_forward_f32_workspace_bytes",
+    "bitlinear_attention_workspace_bytes",
     "bitlinear_attention_decode", "EXPORTED",
 ]
 
@@ -30,6 +31,8 @@ EXPORTED = (
     "bitlinear_forward_f32",
     "bitlinear_forward_residual",
     "bitlinear_forward_f32_residual",
+    "bitlinear_forward_f32_workspace_bytes",
+    "bitlinear_forward_f32_ws",
     "bitlinear_packed5_row_bytes",
     "bitlinear_repack5",
     "bitlinear_forward5",
@@ -70,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward_residual.restype = ci
         L.bitlinear_forward_f32_residual.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, i64, vp, vp]
         L.bitlinear_forward_f32_residual.restype = ci
+        L.bitlinear_forward_f32_workspace_bytes.argtypes = [i64, i64]
+        L.bitlinear_forward_f32_workspace_bytes.restype = ctypes.c_size_t
+        L.bitlinear_forward_f32_ws.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, i64, vp, ci, vp, ctypes.c_size_t, vp]
+        L.bitlinear_forward_f32_ws.restype = ci
         L.bitlinear_packed5_row_bytes.argtypes = [i64]
         L.bitlinear_packed5_row_bytes.restype = i64
         L.bitlinear_repack5.argtypes = [vp, i64, i64, vp, vp]
@@ -210,10 +217,18 @@ def bitlinear_forward(Xq, x_scale, W_packed, gamma, y=None, acc=None, stream=Non
     return (y, acc) if isinstance(acc, torch.Tensor) else y
 
 
+def bitlinear_forward_f32_workspace_bytes(M: int, K: int) -> int:
+    """Workspace bytes of bitlinear_forward_f32_ws (0: none needed)."""
+    return int(lib().bitlinear_forward_f32_workspace_bytes(int(M), int(K)))
+
+
 def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=0, y=None, stream=None,
-                          residual=False):
+                          residual=False, workspace=None, one_launch=False):
     """Fused quantize + product from fp32 activations [M][K] ([M][2K] when act == 2) -> fp32 y [M][N].
-    residual=True adds the product to the given y."""
+    residual=True adds the product to the given y. From 16 tokens on the call goes through
+    bitlinear_forward_f32_ws (quantize into a workspace, then the matrix-core product); the
+    workspace (uint8, at least bitlinear_forward_f32_workspace_bytes(M, K)) is allocated here
+    when not given. one_launch=True calls the one-launch entry whatever M (same result)."""
     import torch
     _need(X, torch.float32, "X", 2)
     _need(W_packed, torch.uint8, "W_packed", 2)
@@ -234,6 +249,17 @@ def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=
             y = torch.empty((M, N), dtype=torch.float32, device=X.device)
         _need(y, torch.float32, "y", shape=(M, N))
         fn, name = lib().bitlinear_forward_f32, "bitlinear_forward_f32"
+    need = bitlinear_forward_f32_workspace_bytes(M, K)
+    if not one_launch and (need > 0 or workspace is not None):
+        if workspace is None:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=X.device)
+        _need(workspace, torch.uint8, "workspace", 1)
+        if workspace.numel() < need:
+            raise ValueError("workspace must hold %d bytes" % need)
+        _check(lib().bitlinear_forward_f32_ws(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(W_packed), _ptr(gamma),
+                                              N, _ptr(y), int(bool(residual)), _ptr(workspace), workspace.numel(),
+                                              _stream(stream)), "bitlinear_forward_f32_ws")
+        return y
     _check(fn(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(W_packed), _ptr(gamma), N, _ptr(y), _stream(stream)),
            name)
     return y

@@ -332,9 +332,8 @@ int forward_impl(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, c
     return launched();
 }
 
-int forward_f32_impl(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
-                     const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int residual,
-                     hipStream_t stream)
+int check_f32_args(const float* X, int64_t M, int64_t K, const float* gain, int act, const uint8_t* W_packed,
+                   const float* gamma, int64_t N, const float* Y)
 {
     if (!X || !W_packed || !gamma || !Y)
         return BITLINEAR_ERR_NULL;
@@ -353,6 +352,25 @@ int forward_f32_impl(const float* X, int64_t M, int64_t K, const float* gain, fl
     for (int i = 0; i < 4; ++i)
         if (overlap(Y, ybytes, ins[i], insz[i]))
             return BITLINEAR_ERR_ALIAS;
+    return BITLINEAR_OK;
+}
+
+// Token counts from which the product runs on the matrix cores (and the fused call with a
+// workspace quantizes first, then multiplies).
+constexpr int64_t kGemmMinTokens = 16;
+
+int64_t round256(int64_t b)
+{
+    return (b + 255) / 256 * 256;
+}
+
+int forward_f32_impl(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
+                     const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int residual,
+                     hipStream_t stream)
+{
+    const int st = check_f32_args(X, M, K, gain, act, W_packed, gamma, N, Y);
+    if (st != BITLINEAR_OK)
+        return st;
     bl::FwdArgs a{};
     a.X = X;
     a.gain = gain;
@@ -546,6 +564,42 @@ int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const f
                                    hipStream_t stream)
 {
     return forward_f32_impl(X, M, K, gain, eps, act, W_packed, gamma, N, Y, 1, stream);
+}
+
+size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t K)
+{
+    if (check_mk(M, K) != BITLINEAR_OK || M < kGemmMinTokens)
+        return 0;
+    return (size_t)(round256(M * K) + round256(M * 4));
+}
+
+int bitlinear_forward_f32_ws(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
+                             const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int residual,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    int st = check_f32_args(X, M, K, gain, act, W_packed, gamma, N, Y);
+    if (st != BITLINEAR_OK)
+        return st;
+    const size_t need = bitlinear_forward_f32_workspace_bytes(M, K);
+    if (need == 0)
+        return forward_f32_impl(X, M, K, gain, eps, act, W_packed, gamma, N, Y, residual, stream);
+    if (!workspace)
+        return BITLINEAR_ERR_NULL;
+    if (workspace_bytes < need)
+        return BITLINEAR_ERR_WORKSPACE;
+    if (!aligned(workspace, 16))
+        return BITLINEAR_ERR_ALIGN;
+    const void* bufs[5] = {X, gain, W_packed, gamma, Y};
+    const int64_t sz[5] = {M * K * 4 * (act == 2 ? 2 : 1), K * 4, N * (K / 4), 4, M * N * 4};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(workspace, (int64_t)need, bufs[i], sz[i]))
+            return BITLINEAR_ERR_ALIAS;
+    int8_t* xq = static_cast<int8_t*>(workspace);
+    float* xs = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(M * K));
+    // both calls accept these arguments (checked above), so nothing is enqueued unless both run
+    if ((st = bitlinear_quantize_act(X, M, K, gain, eps, act, xq, xs, stream)) != BITLINEAR_OK)
+        return st;
+    return forward_impl(xq, xs, M, K, W_packed, gamma, N, Y, nullptr, residual, stream);
 }
 
 int64_t bitlinear_packed5_row_bytes(int64_t K)

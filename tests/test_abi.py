@@ -97,6 +97,37 @@ def test_forward_f32_rejects_before_launch(L):
     assert f(P(a), 1, 64, None, 1e-5, 2, P(3 * a), P(4 * a), 8, P(a + 300), None) == ERR_ALIAS
 
 
+def test_forward_f32_workspace_bytes(L):
+    f = bl.bitlinear_forward_f32_workspace_bytes
+    assert f(1, 64) == 0 and f(15, 256) == 0          # one-launch sizes need none
+    assert f(16, 256) == 4096 + 256                    # codes, then scales, each on 256 bytes
+    assert f(100, 260) == 26112 + 512
+    assert f(2048, 6912) == 2048 * 6912 + 8192
+    assert f(16, 62) == 0 and f(0, 64) == 0 and f(16, (1 << 20) + 4) == 0   # out of range
+
+
+def test_forward_f32_ws_rejects_before_launch(L):
+    f = L.bitlinear_forward_f32_ws
+    a = 1 << 24
+    M, K, N = 16, 256, 8
+    need = bl.bitlinear_forward_f32_workspace_bytes(M, K)
+
+    def call(ws, nbytes, X=P(a), k=K):
+        return f(X, M, k, None, 1e-5, 0, P(3 * a), P(4 * a), N, P(5 * a), 0, ws, nbytes, None)
+
+    assert call(None, need) == ERR_NULL
+    assert call(P(6 * a), need - 1) == ERR_WORKSPACE
+    assert call(P(6 * a + 8), need) == ERR_ALIGN
+    assert call(P(5 * a - 64), need) == ERR_ALIAS      # runs into Y
+    assert call(P(a + 16), need) == ERR_ALIAS          # inside X (M*K*4 bytes)
+    # the one-launch call's own checks come first
+    assert call(P(6 * a), need, k=62) == ERR_SHAPE
+    assert call(P(6 * a), need, X=None) == ERR_NULL
+    # below 16 tokens no workspace is needed: the one-launch checks alone apply
+    g = f(P(a), 4, K, None, 1e-5, 7, P(3 * a), P(4 * a), N, P(5 * a), 0, None, 0, None)
+    assert g == ERR_SHAPE
+
+
 def test_residual_forms_reject_before_launch(L):
     a = 1 << 20
     f = L.bitlinear_forward_residual

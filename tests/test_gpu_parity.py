@@ -160,8 +160,9 @@ def run_gpu(x, w, mode=None, gain=None, relu2=False):
         xq, s = bl.bitlinear_quantize_act(xg, gg, EPS, relu2)
     y, acc = bl.bitlinear_forward(xq, s, packed, gamma, acc=True)
     yf = bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, relu2)
+    y1 = bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, relu2, one_launch=True)
     return dict(packed=down(packed), gamma=down(gamma)[0], xq=down(xq), s=down(s), y=down(y), acc=down(acc),
-                yf=down(yf))
+                yf=down(yf), y1=down(y1))
 
 
 def compare(r, o, norm):
@@ -170,6 +171,7 @@ def compare(r, o, norm):
     assert np.array_equal(r["xq"], o["xq"])
     assert np.array_equal(r["acc"], o["acc"])
     assert np.array_equal(r["y"].view(np.int32), r["yf"].view(np.int32)), "fused != quantize+forward"
+    assert np.array_equal(r["y"].view(np.int32), r["y1"].view(np.int32)), "one-launch fused != quantize+forward"
     if not norm:
         assert np.array_equal(r["s"], o["s"])
         assert np.array_equal(r["y"].view(np.int32), o["y"].view(np.int32))
@@ -272,6 +274,42 @@ RESIDUAL_CASES = [
 ]
 
 
+WS_CASES = [
+    # (M, N, K, mode): token counts that take the workspace path (quantize, then the MFMA
+    # product), incl. ragged tiles, each input kind, and a K the matrix cores do not take
+    (16, 96, 2560, None), (100, 130, 2560, "norm"), (300, 64, 6912, "relu2norm"), (64, 40, 2560, "gatednorm"),
+    (33, 50, 260, "relu2"), (17, 8, 128, "gated"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,mode", WS_CASES)
+def test_forward_f32_workspace(M, N, K, mode):
+    """bitlinear_forward_f32_ws: bit for bit quantize + forward, and the oracle's result
+    (bit-exact on the plain path, within 1e-6 on the subln path); a reused workspace gives
+    the same bits again."""
+    w = latents(N, K, 9600 + N + K)
+    x = make_acts(M, row_len(mode, K), 9700 + M + K, heavy=True)
+    gain, act = pro_args(mode, K, 9800 + K)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    xg, gg = up(x), None if gain is None else up(gain)
+    need = bl.bitlinear_forward_f32_workspace_bytes(M, K)
+    assert need >= M * K + 4 * M
+    ws = torch.full((need + 64,), 0x5A, dtype=torch.uint8, device=DEV)
+    yw = bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, act, workspace=ws)
+    yw2 = bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, act, workspace=ws)
+    xq, s = bl.bitlinear_quantize_act(xg, gg, EPS, act)
+    y = bl.bitlinear_forward(xq, s, packed, gamma)
+    rw, rw2, r = down(yw), down(yw2), down(y)
+    assert np.array_equal(rw.view(np.int32), r.view(np.int32))
+    assert np.array_equal(rw2.view(np.int32), r.view(np.int32))
+    o = oracle.bitlinear(x, w, gain=gain, eps=EPS, relu2=act) if mode else oracle.bitlinear(x, w)
+    if gain is None:
+        assert np.array_equal(rw.view(np.int32), o["y"].view(np.int32))
+    else:
+        yo = o["y"].astype(np.float64)
+        assert (np.abs(rw.astype(np.float64) - yo) <= 1e-6 * np.abs(yo)).all()
+
+
 def oracle_residual(y0, y_ora):
     return (y0.astype(np.float32) + y_ora.astype(np.float32)).astype(np.float32)
 
@@ -298,11 +336,14 @@ def test_residual_parity(M, N, K, mode):
     bl.bitlinear_forward(xq, s, packed, gamma, y=ya, residual=True)
     yb = up(y0)
     bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, act, y=yb, residual=True)
+    yc = up(y0)
+    bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, act, y=yc, residual=True, one_launch=True)
     plain = bl.bitlinear_forward(xq, s, packed, gamma)
-    ra, rb, rp = down(ya), down(yb), down(plain)
+    ra, rb, rc, rp = down(ya), down(yb), down(yc), down(plain)
     same = oracle_residual(y0, rp)
     assert np.array_equal(ra.view(np.int32), same.view(np.int32))
     assert np.array_equal(rb.view(np.int32), same.view(np.int32))
+    assert np.array_equal(rc.view(np.int32), same.view(np.int32))
     if gain is None:
         assert np.array_equal(ra.view(np.int32), expect.view(np.int32))
     else:
