@@ -599,17 +599,27 @@ def run_extra(torch, bl, datagen, dev, mats2b):
 
 def run_prefill(torch, bl, datagen, dev, M):
     """The pre-quantized product on the 2B shapes at M tokens (int8 MFMA GEMM): time per
-    launch (graph of 10, two weight copies) and int8 TOPS against the 5 POPS dense peak."""
+    launch (graph of 10, two weight copies) and int8 TOPS against the 5 POPS dense peak; the
+    quantization launch on its own (GB/s of its algorithmic bytes against 8 TB/s; the fp32
+    input is one buffer, so it may come from the 256 MB MALL) and the fused call with a
+    workspace (quantization, then the product)."""
     r = {}
     for i, (name, N, K, mode) in enumerate(LAYER_2B):
         m = Mat(torch, bl, datagen, 4, i + 4 * (M > 512), name, N, K, mode, M, 2, dev)
         m.x = datagen.heavy_channel_acts_torch(M, K, datagen.stream_id(4, 1, i, 1), dev)
         m.prequant(bl)
         a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), 2, 10)
+        q = time_kernel(torch, lambda c, m=m: m.prequant(bl), 1, 10)
+        ws = torch.empty((bl.bitlinear_forward_f32_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+        f = time_kernel(torch, lambda c, m=m: bl.bitlinear_forward_f32(m.x, m.copies[c], m.gamma, m.gain, EPS,
+                                                                       m.relu2, y=m.y, workspace=ws), 2, 10)
         ops = 2.0 * M * N * K
+        qb = 4 * M * K + (4 * K if m.gain is not None else 0) + M * K + 4 * M
         r[name] = {"us": round(a * 1e6, 1), "TOPS": round(ops / a / 1e12, 2),
-                   "frac_int8_peak": round(ops / a / 1e12 / INT8_PEAK_TOPS, 4)}
-        del m
+                   "frac_int8_peak": round(ops / a / 1e12 / INT8_PEAK_TOPS, 4),
+                   "quantize_us": round(q * 1e6, 1), "quantize_GB/s": round(qb / q / 1e9, 1),
+                   "quantize_frac_hbm": round(qb / q / 1e9 / HBM_PEAK_GBS, 4), "fused_us": round(f * 1e6, 1)}
+        del m, ws
     log("extra prefill M=%d: %s" % (M, r))
     return r
 

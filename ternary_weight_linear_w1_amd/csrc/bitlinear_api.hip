@@ -536,8 +536,16 @@ int bitlinear_quantize_act(const float* X, int64_t M, int64_t K, const float* ga
         return BITLINEAR_ERR_ALIAS;
     bl::QuantArgs a{X, gain, Xq, x_scale, M, (int)K, eps, act};
     const int64_t max_blocks = int64_t(cu_count()) * 64;
-    hipLaunchKernelGGL(bl::quantize_act_kernel, dim3((unsigned)(M < max_blocks ? M : max_blocks)), dim3(256), 0,
-                       stream, a);
+    const dim3 grid((unsigned)(M < max_blocks ? M : max_blocks));
+    const int64_t per_thread = (K / 16 + 255) / 256;   // 16-element units per thread
+    if (per_thread <= 1)
+        hipLaunchKernelGGL(bl::quantize_act_kernel<1>, grid, dim3(256), 0, stream, a);
+    else if (per_thread <= 2)
+        hipLaunchKernelGGL(bl::quantize_act_kernel<2>, grid, dim3(256), 0, stream, a);
+    else if (per_thread <= 4)
+        hipLaunchKernelGGL(bl::quantize_act_kernel<4>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(bl::quantize_act_kernel<8>, grid, dim3(256), 0, stream, a);
     return launched();
 }
 
