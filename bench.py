@@ -119,8 +119,8 @@ class Mat:
     def prequant(self, bl):
         bl.bitlinear_quantize_act(self.x, self.gain, EPS, self.relu2, xq=self.xq, scale=self.s)
 
-    def forward(self, bl, c):
-        bl.bitlinear_forward(self.xq, self.s, self.copies[c], self.gamma, y=self.y)
+    def forward(self, bl, c, workspace=None, split=True):
+        bl.bitlinear_forward(self.xq, self.s, self.copies[c], self.gamma, y=self.y, workspace=workspace, split=split)
 
     def bytes(self, fused=True):
         return layer_bytes(self.N, self.K, self.M, self.mode, fused)
@@ -538,8 +538,9 @@ def run_extra(torch, bl, datagen, dev, mats2b):
         res["2B_M%d" % M] = r
         log("extra 2B M=%d: %s" % (M, r))
     torch.cuda.empty_cache()
-    # ---- 100B-shaped slice at M = 1 (fused) and M = 64 (pre-quantized)
-    for M in (1, 64):
+    # ---- 100B-shaped slice at M = 1 (fused), M = 32 and 64 (pre-quantized; at 32 tokens the
+    #      down projection's K is split across blocks, timed beside the unsplit product)
+    for M in (1, 32, 64):
         r = {}
         for i, (name, N, K, mode) in enumerate(LAYER_100B):
             C = n_copies(N * K // 4)
@@ -560,9 +561,15 @@ def run_extra(torch, bl, datagen, dev, mats2b):
                            "quantize_us": round(q * 1e6, 2), "TOPS_forward": round(ops / f / 1e12, 2)}
             else:
                 m.prequant(bl)
-                a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), C, 100)
+                need = bl.bitlinear_forward_workspace_bytes(M, N, K)
+                ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+                a = time_kernel(torch, lambda c, m=m: m.forward(bl, c, ws), C, 100)
                 b = m.bytes(fused=False)
                 r[name] = {"us": round(a * 1e6, 2), "GB/s": round(b / a / 1e9, 1), "TOPS": round(ops / a / 1e12, 2)}
+                if need:
+                    u = time_kernel(torch, lambda c, m=m: m.forward(bl, c, split=False), C, 100)
+                    r[name].update({"k_slices": need // (4 * M * N), "unsplit_us": round(u * 1e6, 2)})
+                del ws
             del m
             torch.cuda.empty_cache()
         res["100B_M%d" % M] = r
@@ -610,7 +617,7 @@ def run_prefill(torch, bl, datagen, dev, M):
         m.prequant(bl)
         a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), 2, 10)
         q = time_kernel(torch, lambda c, m=m: m.prequant(bl), 1, 10)
-        ws = torch.empty((bl.bitlinear_forward_f32_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+        ws = torch.empty((bl.bitlinear_forward_f32_workspace_bytes(M, N, K),), dtype=torch.uint8, device=dev)
         f = time_kernel(torch, lambda c, m=m: bl.bitlinear_forward_f32(m.x, m.copies[c], m.gamma, m.gain, EPS,
                                                                        m.relu2, y=m.y, workspace=ws), 2, 10)
         ops = 2.0 * M * N * K

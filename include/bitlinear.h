@@ -157,10 +157,10 @@ int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const f
  * One launch converts the input inside the product only while the tokens fit a few
  * token tiles of the decode product; from 16 tokens on, every tile would read all the
  * weights again. This entry then quantizes into the workspace and runs the matrix-core
- * product: bit for bit bitlinear_quantize_act followed by bitlinear_forward (or
- * bitlinear_forward_residual), the same result the one-launch call gives.
+ * product: bit for bit bitlinear_quantize_act followed by bitlinear_forward_ws (or its
+ * residual form), the same result the one-launch call gives.
  *
- *   workspace        device scratch of at least bitlinear_forward_f32_workspace_bytes(M, K)
+ *   workspace        device scratch of at least bitlinear_forward_f32_workspace_bytes(M, N, K)
  *                    bytes, 16-byte aligned, overlapping no argument; its contents after
  *                    the call are unspecified; calls that may run concurrently need
  *                    distinct workspaces. When that size is 0 (M < 16, or sizes out of
@@ -171,10 +171,37 @@ int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const f
  * when one is needed. bitlinear_forward_f32_workspace_bytes returns 0 for sizes out of
  * range.
  */
-size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t K);
+size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int bitlinear_forward_f32_ws(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
                              const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int residual,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The product with a caller workspace (the same operation and result as bitlinear_forward,
+ * or bitlinear_forward_residual when residual != 0; "BitNet b1.58 深度解析" s.2.3).
+ *
+ * With few tokens (16 to 32) and long rows (K >= 16384) the matrix-core product has too
+ * few output tiles to occupy the GPU and each tile walks all of K in sequence. With a
+ * workspace the K range is cut into up to 8 slices computed by separate blocks, each
+ * writing its exact int32 partial sum to the workspace; a second launch adds the slices
+ * (integer addition: the same accumulator in any order) and applies the rescale of the
+ * unsplit product, so the result is bit for bit that of bitlinear_forward. The partials
+ * then stay within a quarter of the packed weight bytes; for other sizes the workspace
+ * size is 0 and the call is bitlinear_forward's.
+ *
+ *   workspace   device scratch of at least bitlinear_forward_workspace_bytes(M, N, K)
+ *               bytes (the slices' int32 partials), 16-byte aligned, overlapping no
+ *               argument; contents unspecified after the call; concurrent calls need
+ *               distinct workspaces. When that size is 0 (no split for these sizes) the
+ *               workspace is not used and may be NULL.
+ * Other arguments, layouts and errors as in bitlinear_forward; additionally
+ * BITLINEAR_ERR_NULL / BITLINEAR_ERR_WORKSPACE for a missing or short workspace when one
+ * is needed. bitlinear_forward_workspace_bytes returns 0 for sizes out of range.
+ */
+size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int bitlinear_forward_ws(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed,
+                         const float* gamma, int64_t N, float* Y, int32_t* acc, int residual, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Five ternary codes per byte (1.6 bits per weight) instead of four: "微软AI大模型炸场"

@@ -18,7 +18,7 @@ from ._build import LIB as _LIB_PATH
 __all__ = [
     "BitLinearError", "lib", "status_string", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
     "bitlinear_quantize_act", "bitlinear_forward", "bitlinear_forward_f32", "bitlinear_forward_f32_workspace_bytes",
-    "bitlinear_attention_workspace_bytes",
+    "bitlinear_forward_workspace_bytes", "bitlinear_attention_workspace_bytes",
     "bitlinear_attention_decode", "EXPORTED",
 ]
 
@@ -33,6 +33,8 @@ EXPORTED = (
     "bitlinear_forward_f32_residual",
     "bitlinear_forward_f32_workspace_bytes",
     "bitlinear_forward_f32_ws",
+    "bitlinear_forward_workspace_bytes",
+    "bitlinear_forward_ws",
     "bitlinear_packed5_row_bytes",
     "bitlinear_repack5",
     "bitlinear_forward5",
@@ -73,10 +75,14 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward_residual.restype = ci
         L.bitlinear_forward_f32_residual.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, i64, vp, vp]
         L.bitlinear_forward_f32_residual.restype = ci
-        L.bitlinear_forward_f32_workspace_bytes.argtypes = [i64, i64]
+        L.bitlinear_forward_f32_workspace_bytes.argtypes = [i64, i64, i64]
         L.bitlinear_forward_f32_workspace_bytes.restype = ctypes.c_size_t
         L.bitlinear_forward_f32_ws.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, i64, vp, ci, vp, ctypes.c_size_t, vp]
         L.bitlinear_forward_f32_ws.restype = ci
+        L.bitlinear_forward_workspace_bytes.argtypes = [i64, i64, i64]
+        L.bitlinear_forward_workspace_bytes.restype = ctypes.c_size_t
+        L.bitlinear_forward_ws.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, ci, vp, ctypes.c_size_t, vp]
+        L.bitlinear_forward_ws.restype = ci
         L.bitlinear_packed5_row_bytes.argtypes = [i64]
         L.bitlinear_packed5_row_bytes.restype = i64
         L.bitlinear_repack5.argtypes = [vp, i64, i64, vp, vp]
@@ -185,9 +191,18 @@ def bitlinear_quantize_act(X, gain=None, eps: float = 1e-5, act=0, xq=None, scal
     return xq, scale
 
 
-def bitlinear_forward(Xq, x_scale, W_packed, gamma, y=None, acc=None, stream=None, residual=False):
+def bitlinear_forward_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes of bitlinear_forward_ws (0: no split for these sizes)."""
+    return int(lib().bitlinear_forward_workspace_bytes(int(M), int(N), int(K)))
+
+
+def bitlinear_forward(Xq, x_scale, W_packed, gamma, y=None, acc=None, stream=None, residual=False,
+                      workspace=None, split=True):
     """int8 activations + packed ternary weights -> fp32 y [M][N] (and int32 acc if given).
-    residual=True adds the product to the given y (no acc)."""
+    residual=True adds the product to the given y (no acc). With 16 to 32 tokens and long
+    rows the call goes through bitlinear_forward_ws (K split across blocks; the workspace, uint8 of at least
+    bitlinear_forward_workspace_bytes(M, N, K), is allocated here when not given);
+    split=False calls bitlinear_forward / bitlinear_forward_residual (same result)."""
     import torch
     _need(Xq, torch.int8, "Xq", 2)
     _need(W_packed, torch.uint8, "W_packed", 2)
@@ -201,25 +216,37 @@ def bitlinear_forward(Xq, x_scale, W_packed, gamma, y=None, acc=None, stream=Non
         if y is None or acc is not None:
             raise ValueError("residual needs y and takes no acc")
         _need(y, torch.float32, "y", shape=(M, N))
+    else:
+        if y is None:
+            y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+        _need(y, torch.float32, "y", shape=(M, N))
+        if acc is True:
+            acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+        if isinstance(acc, torch.Tensor):
+            _need(acc, torch.int32, "acc", shape=(M, N))
+    accp = _ptr(acc if isinstance(acc, torch.Tensor) else None)
+    need = bitlinear_forward_workspace_bytes(M, N, K)
+    if split and (need > 0 or workspace is not None):
+        if workspace is None:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=Xq.device)
+        _need(workspace, torch.uint8, "workspace", 1)
+        if workspace.numel() < need:
+            raise ValueError("workspace must hold %d bytes" % need)
+        _check(lib().bitlinear_forward_ws(_ptr(Xq), _ptr(x_scale), M, K, _ptr(W_packed), _ptr(gamma), N, _ptr(y), accp,
+                                          int(bool(residual)), _ptr(workspace), workspace.numel(), _stream(stream)),
+               "bitlinear_forward_ws")
+    elif residual:
         _check(lib().bitlinear_forward_residual(_ptr(Xq), _ptr(x_scale), M, K, _ptr(W_packed), _ptr(gamma), N,
                                                 _ptr(y), _stream(stream)), "bitlinear_forward_residual")
-        return y
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
-    _need(y, torch.float32, "y", shape=(M, N))
-    if acc is True:
-        acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
-    if isinstance(acc, torch.Tensor):
-        _need(acc, torch.int32, "acc", shape=(M, N))
-    _check(lib().bitlinear_forward(_ptr(Xq), _ptr(x_scale), M, K, _ptr(W_packed), _ptr(gamma), N, _ptr(y),
-                                   _ptr(acc if acc is not None and acc is not False else None), _stream(stream)),
-           "bitlinear_forward")
+    else:
+        _check(lib().bitlinear_forward(_ptr(Xq), _ptr(x_scale), M, K, _ptr(W_packed), _ptr(gamma), N, _ptr(y), accp,
+                                       _stream(stream)), "bitlinear_forward")
     return (y, acc) if isinstance(acc, torch.Tensor) else y
 
 
-def bitlinear_forward_f32_workspace_bytes(M: int, K: int) -> int:
+def bitlinear_forward_f32_workspace_bytes(M: int, N: int, K: int) -> int:
     """Workspace bytes of bitlinear_forward_f32_ws (0: none needed)."""
-    return int(lib().bitlinear_forward_f32_workspace_bytes(int(M), int(K)))
+    return int(lib().bitlinear_forward_f32_workspace_bytes(int(M), int(N), int(K)))
 
 
 def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=0, y=None, stream=None,
@@ -227,7 +254,7 @@ def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=
     """Fused quantize + product from fp32 activations [M][K] ([M][2K] when act == 2) -> fp32 y [M][N].
     residual=True adds the product to the given y. From 16 tokens on the call goes through
     bitlinear_forward_f32_ws (quantize into a workspace, then the matrix-core product); the
-    workspace (uint8, at least bitlinear_forward_f32_workspace_bytes(M, K)) is allocated here
+    workspace (uint8, at least bitlinear_forward_f32_workspace_bytes(M, N, K)) is allocated here
     when not given. one_launch=True calls the one-launch entry whatever M (same result)."""
     import torch
     _need(X, torch.float32, "X", 2)
@@ -249,7 +276,7 @@ def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=
             y = torch.empty((M, N), dtype=torch.float32, device=X.device)
         _need(y, torch.float32, "y", shape=(M, N))
         fn, name = lib().bitlinear_forward_f32, "bitlinear_forward_f32"
-    need = bitlinear_forward_f32_workspace_bytes(M, K)
+    need = bitlinear_forward_f32_workspace_bytes(M, N, K)
     if not one_launch and (need > 0 or workspace is not None):
         if workspace is None:
             workspace = torch.empty((need,), dtype=torch.uint8, device=X.device)

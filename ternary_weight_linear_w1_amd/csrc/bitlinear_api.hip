@@ -213,9 +213,56 @@ void launch_gemm(const bl::FwdArgs& f, hipStream_t stream)
 {
     const int64_t tiles_m = (f.M + BM - 1) / BM, tiles_n = (f.N + BN - 1) / BN;
     bl::GemmArgs a{f.Xq, f.xscale, f.W, f.gamma, f.Y, f.acc, (int)f.M, (int)f.N, f.K, f.residual,
-                   bl::gemm_region_split(tiles_m, tiles_n, BM, BN, f.K)};
+                   bl::gemm_region_split(tiles_m, tiles_n, BM, BN, f.K), nullptr, 1, f.K};
     const int64_t tiles = tiles_m * tiles_n;
     hipLaunchKernelGGL((bl::gemm_mfma_kernel<BM, BN, WM, WN, P, BK, WK>), dim3((unsigned)tiles), dim3(256), 0,
+                       stream, a);
+}
+
+int64_t round256(int64_t b)
+{
+    return (b + 255) / 256 * 256;
+}
+
+// Split K for few tokens (the product with a caller workspace): 32 x 128 tiles, K steps of
+// 256, up to 8 slices of at least 4 steps each, aiming at about 1024 blocks (four resident
+// per CU on 256 CUs). A pure function of the sizes, so the workspace size needs no device.
+constexpr int kSplitStep = 256;
+
+// K slices of the split product (1: no split). Measured on MI355X against the unsplit
+// kernel at 16..128 tokens over the 2B and 100B shapes: splitting pays only where few token
+// tiles meet a long K loop (K >= 16384: about 1.45x on the 100B down projection at 16 and
+// 32 tokens). At 64 tokens and beyond, or with shorter rows, the int32 partials (written
+// and read once more) and the second launch cost more than the shorter loop gains. Up to 8
+// slices of at least 4 K steps, aiming at about 1024 blocks; the partials are then at most
+// a quarter of the packed weight bytes (16 M s <= K / 4).
+int splitk_slices(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 16 || M > 32 || (K % 64) != 0 || K < 16384)
+        return 1;
+    const int64_t tiles = ((M + 31) / 32) * ((N + 127) / 128);
+    const int64_t nk = (K + kSplitStep - 1) / kSplitStep;
+    int64_t s = 1024 / tiles;
+    if (s > nk / 4)
+        s = nk / 4;
+    if (s > 8)
+        s = 8;
+    return s < 2 ? 1 : (int)s;
+}
+
+void launch_gemm_split(const bl::FwdArgs& f, int32_t* part, int slices, hipStream_t stream)
+{
+    const int64_t tiles_m = (f.M + 31) / 32, tiles_n = (f.N + 127) / 128;
+    const int64_t nk = (f.K + kSplitStep - 1) / kSplitStep;
+    const int kslice = (int)((nk + slices - 1) / slices) * kSplitStep;
+    const int used = (int)((f.K + kslice - 1) / kslice);   // slices that hold columns
+    bl::GemmArgs a{f.Xq, f.xscale, f.W, f.gamma, f.Y, f.acc, (int)f.M, (int)f.N, f.K, f.residual, 1,
+                   part, used, kslice};
+    hipLaunchKernelGGL((bl::gemm_mfma_kernel<32, 128, 1, 4, 2, kSplitStep>), dim3((unsigned)(tiles_m * tiles_n * used)),
+                       dim3(256), 0, stream, a);
+    const int64_t total = f.M * f.N;
+    const int64_t blocks = (total + 255) / 256, cap = int64_t(cu_count()) * 8;
+    hipLaunchKernelGGL(bl::gemm_splitk_reduce_kernel, dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(256), 0,
                        stream, a);
 }
 
@@ -292,8 +339,8 @@ void dispatch_forward(const bl::FwdArgs& a, bool chunk_ok, hipStream_t stream)
     launch_generic<FUSED>(a, stream);
 }
 
-int forward_impl(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed,
-                 const float* gamma, int64_t N, float* Y, int32_t* acc, int residual, hipStream_t stream)
+int check_fwd_args(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed,
+                   const float* gamma, int64_t N, const float* Y, const int32_t* acc)
 {
     if (!Xq || !x_scale || !W_packed || !gamma || !Y)
         return BITLINEAR_ERR_NULL;
@@ -315,6 +362,18 @@ int forward_impl(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, c
             return BITLINEAR_ERR_ALIAS;
     if (overlap(Y, ybytes, acc, ybytes))
         return BITLINEAR_ERR_ALIAS;
+    return BITLINEAR_OK;
+}
+
+// The product; with `part` (a workspace of splitk_slices(M, N, K) * M * N int32) few tokens
+// take the split-K matrix-core path.
+int forward_impl(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed,
+                 const float* gamma, int64_t N, float* Y, int32_t* acc, int residual, hipStream_t stream,
+                 int32_t* part = nullptr)
+{
+    const int st = check_fwd_args(Xq, x_scale, M, K, W_packed, gamma, N, Y, acc);
+    if (st != BITLINEAR_OK)
+        return st;
     bl::FwdArgs a{};
     a.Xq = Xq;
     a.xscale = x_scale;
@@ -327,9 +386,19 @@ int forward_impl(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, c
     a.K = (int)K;
     a.residual = residual;
     const bool chunk_ok = (K % 64) == 0 && aligned(W_packed, 16) && aligned(Xq, 16);
-    if (!(chunk_ok && dispatch_gemm(a, stream)))
+    const int slices = splitk_slices(M, N, K);
+    if (part && chunk_ok && slices > 1 && ((M + 31) / 32) * ((N + 127) / 128) * slices < INT32_MAX)
+        launch_gemm_split(a, part, slices, stream);
+    else if (!(chunk_ok && dispatch_gemm(a, stream)))
         dispatch_forward<false>(a, chunk_ok, stream);
     return launched();
+}
+
+// Bytes of the split-K partials of the product with a workspace (0: no split).
+int64_t split_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const int s = splitk_slices(M, N, K);
+    return s > 1 ? round256((int64_t)s * M * N * 4) : 0;
 }
 
 int check_f32_args(const float* X, int64_t M, int64_t K, const float* gain, int act, const uint8_t* W_packed,
@@ -359,10 +428,6 @@ int check_f32_args(const float* X, int64_t M, int64_t K, const float* gain, int 
 // workspace quantizes first, then multiplies).
 constexpr int64_t kGemmMinTokens = 16;
 
-int64_t round256(int64_t b)
-{
-    return (b + 255) / 256 * 256;
-}
 
 int forward_f32_impl(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
                      const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int residual,
@@ -574,11 +639,43 @@ int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const f
     return forward_f32_impl(X, M, K, gain, eps, act, W_packed, gamma, N, Y, 1, stream);
 }
 
-size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t K)
+size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    if (check_mk(M, K) != BITLINEAR_OK || M < kGemmMinTokens)
+    if (check_mk(M, K) != BITLINEAR_OK || M < kGemmMinTokens || check_nk(N, K) != BITLINEAR_OK || M > kMaxElems / N)
         return 0;
-    return (size_t)(round256(M * K) + round256(M * 4));
+    return (size_t)(round256(M * K) + round256(M * 4) + split_bytes(M, N, K));
+}
+
+size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (check_mk(M, K) != BITLINEAR_OK || check_nk(N, K) != BITLINEAR_OK || M > kMaxElems / N)
+        return 0;
+    return (size_t)split_bytes(M, N, K);
+}
+
+int bitlinear_forward_ws(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* W_packed,
+                         const float* gamma, int64_t N, float* Y, int32_t* acc, int residual, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream)
+{
+    int st = check_fwd_args(Xq, x_scale, M, K, W_packed, gamma, N, Y, acc);
+    if (st != BITLINEAR_OK)
+        return st;
+    const size_t need = bitlinear_forward_workspace_bytes(M, N, K);
+    if (need == 0)
+        return forward_impl(Xq, x_scale, M, K, W_packed, gamma, N, Y, acc, residual ? 1 : 0, stream);
+    if (!workspace)
+        return BITLINEAR_ERR_NULL;
+    if (workspace_bytes < need)
+        return BITLINEAR_ERR_WORKSPACE;
+    if (!aligned(workspace, 16))
+        return BITLINEAR_ERR_ALIGN;
+    const void* bufs[6] = {Xq, x_scale, W_packed, gamma, Y, acc};
+    const int64_t sz[6] = {M * K, M * 4, N * (K / 4), 4, M * N * 4, M * N * 4};
+    for (int i = 0; i < 6; ++i)
+        if (overlap(workspace, (int64_t)need, bufs[i], sz[i]))
+            return BITLINEAR_ERR_ALIAS;
+    return forward_impl(Xq, x_scale, M, K, W_packed, gamma, N, Y, acc, residual ? 1 : 0, stream,
+                        static_cast<int32_t*>(workspace));
 }
 
 int bitlinear_forward_f32_ws(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
@@ -588,7 +685,7 @@ int bitlinear_forward_f32_ws(const float* X, int64_t M, int64_t K, const float* 
     int st = check_f32_args(X, M, K, gain, act, W_packed, gamma, N, Y);
     if (st != BITLINEAR_OK)
         return st;
-    const size_t need = bitlinear_forward_f32_workspace_bytes(M, K);
+    const size_t need = bitlinear_forward_f32_workspace_bytes(M, N, K);
     if (need == 0)
         return forward_f32_impl(X, M, K, gain, eps, act, W_packed, gamma, N, Y, residual, stream);
     if (!workspace)
@@ -604,10 +701,13 @@ int bitlinear_forward_f32_ws(const float* X, int64_t M, int64_t K, const float* 
             return BITLINEAR_ERR_ALIAS;
     int8_t* xq = static_cast<int8_t*>(workspace);
     float* xs = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(M * K));
+    int32_t* part = split_bytes(M, N, K) > 0
+                        ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + round256(M * K) + round256(M * 4))
+                        : nullptr;
     // both calls accept these arguments (checked above), so nothing is enqueued unless both run
     if ((st = bitlinear_quantize_act(X, M, K, gain, eps, act, xq, xs, stream)) != BITLINEAR_OK)
         return st;
-    return forward_impl(xq, xs, M, K, W_packed, gamma, N, Y, nullptr, residual, stream);
+    return forward_impl(xq, xs, M, K, W_packed, gamma, N, Y, nullptr, residual ? 1 : 0, stream, part);
 }
 
 int64_t bitlinear_packed5_row_bytes(int64_t K)

@@ -39,6 +39,12 @@ struct GemmArgs {
     int K;
     int residual;         // 1: Y[m][n] = fl32(Y[m][n] + y[m][n])
     int gm;               // tile-grid regions along M (1, 2, 4 or 8; 8 / gm along N)
+    // Split K (few tokens): block b takes K slice b % ksplit (kslice columns, a multiple of
+    // the K step) of tile b / ksplit and writes its exact int32 partial to
+    // part[slice][M][N]; gemm_splitk_reduce_kernel then sums the slices and rescales.
+    int32_t* part;        // null: no split, the block writes y itself
+    int ksplit;           // 1 without a split
+    int kslice;
 };
 
 // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous range of tiles
@@ -141,7 +147,12 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     int tm, tn;
-    region_tile(xcd_tile(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, a.gm, tm, tn);
+    const int slice = a.part ? (int)(blockIdx.x % a.ksplit) : 0;
+    const int bid = a.part ? (int)(blockIdx.x / a.ksplit) : (int)blockIdx.x;
+    region_tile(xcd_tile(bid, tiles_m * tiles_n), tiles_m, tiles_n, a.gm, tm, tn);
+    // this block's K columns: [kbeg, kbeg + klen)
+    const int kbeg = a.part ? slice * a.kslice : 0;
+    const int klen = a.part ? ((K - kbeg) < a.kslice ? (K - kbeg) : a.kslice) : K;
     const int m0 = tm * BM;
     const int n0 = tn * BN;
 
@@ -180,12 +191,12 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
     auto load = [&](u32x4 (&ad)[AU], u32x4 (&bd)[FN][BH], int k0) {
 #pragma unroll
         for (int i = 0; i < AU; ++i)
-            ad[i] = buf_load16(ra, aoff[i], k0);
+            ad[i] = buf_load16(ra, aoff[i], kbeg + k0);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
             for (int h = 0; h < BH; ++h)
-                bd[fn][h] = buf_load16(rb, boff[fn], (k0 >> 2) + 32 * h);
+                bd[fn][h] = buf_load16(rb, boff[fn], ((kbeg + k0) >> 2) + 32 * h);
     };
     // The last step may extend past K (K % BK is a multiple of 64): activations loaded
     // from beyond the row end belong to the next row and are replaced by zeros, which also
@@ -216,12 +227,12 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
             for (int r = 0; r < 16; ++r)
                 C[fm][fn][r] = 0;
 
-    const int nk = (K + SK - 1) / SK;
+    const int nk = (klen + SK - 1) / SK;
 #pragma unroll
     for (int s = 0; s < P; ++s)
         if (s < nk)
             load(areg[s], breg[s], s * SK);
-    store_a(areg[0], 0, K, true);
+    store_a(areg[0], 0, klen, true);
     __syncthreads();
 
     // One K step on ring slot s: unpack its weights (the slot is refilled right after),
@@ -264,7 +275,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
                 for (int fm = 0; fm < FM; ++fm)
                     C[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks][fm], bf[ks][fn], C[fm][fn], 0, 0, 0);
         if (stage)
-            store_a(areg[(s + 1) % P], buf ^ 1, K - (it + 1) * SK, tail);
+            store_a(areg[(s + 1) % P], buf ^ 1, klen - (it + 1) * SK, tail);
         __syncthreads();
     };
 
@@ -331,6 +342,26 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
 
     // C layout of a 32x32 tile: lane l, register r -> column l % 32,
     // row 8 (r / 4) + 4 (l / 32) + r % 4. Each row's offset and scale are read once.
+    if (a.part) {   // split K: the exact int32 partial of this slice
+        int32_t* pt = a.part + (int64_t)slice * M * N;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * TM + fm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int m = m0 + row;
+                if (m < M) {
+                    const int32_t off = rsum[row];
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        const int n = n0 + wn * TN + fn * 32 + (lane & 31);
+                        if (n < N)
+                            pt[(int64_t)m * N + n] = C[fm][fn][r] - off;
+                    }
+                }
+            }
+        return;
+    }
     //
     // Common case (whole tile inside N, plain output, no int32 copy, 32-bit byte offsets):
     // buffer stores with the row's byte offset computed once and the 32-column step as the
@@ -379,6 +410,25 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a)
                 }
             }
         }
+    }
+}
+
+// Sum of the K slices' int32 partials and the product's epilogue, as the unsplit kernel
+// writes it: y = fl32(fl32(acc) * fl32(gamma / s_m)), added into Y with residual.
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(GemmArgs a)
+{
+    const int64_t total = (int64_t)a.M * a.N;
+    const int64_t slice = total;
+    for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+        int32_t v = 0;
+        for (int s = 0; s < a.ksplit; ++s)
+            v += a.part[s * slice + o];
+        const int m = (int)(o / a.N);
+        const float c = *a.gamma / a.xscale[m];
+        const float yv = (float)v * c;
+        a.Y[o] = a.residual ? a.Y[o] + yv : yv;
+        if (a.acc)
+            a.acc[o] = v;
     }
 }
 

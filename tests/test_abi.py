@@ -97,20 +97,36 @@ def test_forward_f32_rejects_before_launch(L):
     assert f(P(a), 1, 64, None, 1e-5, 2, P(3 * a), P(4 * a), 8, P(a + 300), None) == ERR_ALIAS
 
 
+def test_forward_workspace_bytes(L):
+    f = bl.bitlinear_forward_workspace_bytes
+    # K split for 16..32 tokens and K >= 16384: up to 8 slices of >= 4 K steps of 256,
+    # about 1024 blocks; slices x M x N int32 partials
+    assert f(16, 8192, 28672) == 8 * 16 * 8192 * 4      # 64 tiles of 32 x 128: capped at 8
+    assert f(32, 8192, 28672) == 8 * 32 * 8192 * 4
+    assert f(32, 40000, 16384) == 3 * 32 * 40000 * 4    # 313 tiles: 1024 / 313 = 3 slices
+    assert f(32, 20000, 16384) == 6 * 32 * 20000 * 4    # 157 tiles: 6 slices
+    assert f(20, 64, 16384) == 8 * 20 * 64 * 4          # 64 K steps: 16 of 4, capped at 8
+    assert f(16, 96, 2560) == 0 and f(32, 10240, 8192) == 0            # short rows: no split
+    assert f(15, 8192, 28672) == 0 and f(33, 8192, 28672) == 0         # token range
+    assert f(16, 128, 16400) == 0                       # K % 64
+    assert f(0, 64, 64) == 0 and f(16, 64, 62) == 0                    # out of range
+
+
 def test_forward_f32_workspace_bytes(L):
     f = bl.bitlinear_forward_f32_workspace_bytes
-    assert f(1, 64) == 0 and f(15, 256) == 0          # one-launch sizes need none
-    assert f(16, 256) == 4096 + 256                    # codes, then scales, each on 256 bytes
-    assert f(100, 260) == 26112 + 512
-    assert f(2048, 6912) == 2048 * 6912 + 8192
-    assert f(16, 62) == 0 and f(0, 64) == 0 and f(16, (1 << 20) + 4) == 0   # out of range
+    assert f(1, 96, 64) == 0 and f(15, 96, 256) == 0    # one-launch sizes need none
+    assert f(16, 8, 256) == 4096 + 256                  # codes, then scales, each on 256 bytes
+    assert f(100, 130, 260) == 26112 + 512
+    assert f(2048, 6912, 6912) == 2048 * 6912 + 8192
+    assert f(32, 8192, 28672) == 32 * 28672 + 256 + 8 * 32 * 8192 * 4   # and the K-split partials
+    assert f(16, 8, 62) == 0 and f(0, 8, 64) == 0 and f(16, 8, (1 << 20) + 4) == 0   # out of range
 
 
 def test_forward_f32_ws_rejects_before_launch(L):
     f = L.bitlinear_forward_f32_ws
     a = 1 << 24
     M, K, N = 16, 256, 8
-    need = bl.bitlinear_forward_f32_workspace_bytes(M, K)
+    need = bl.bitlinear_forward_f32_workspace_bytes(M, N, K)
 
     def call(ws, nbytes, X=P(a), k=K):
         return f(X, M, k, None, 1e-5, 0, P(3 * a), P(4 * a), N, P(5 * a), 0, ws, nbytes, None)
@@ -126,6 +142,24 @@ def test_forward_f32_ws_rejects_before_launch(L):
     # below 16 tokens no workspace is needed: the one-launch checks alone apply
     g = f(P(a), 4, K, None, 1e-5, 7, P(3 * a), P(4 * a), N, P(5 * a), 0, None, 0, None)
     assert g == ERR_SHAPE
+
+
+def test_forward_ws_rejects_before_launch(L):
+    f = L.bitlinear_forward_ws
+    a = 1 << 26
+    M, K, N = 32, 16384, 256
+    need = bl.bitlinear_forward_workspace_bytes(M, N, K)
+    assert need > 0
+
+    def call(ws, nbytes, Xq=P(a), acc=None):
+        return f(Xq, P(2 * a), M, K, P(3 * a), P(4 * a), N, P(5 * a), acc, 0, ws, nbytes, None)
+
+    assert call(None, need) == ERR_NULL
+    assert call(P(6 * a), need - 4) == ERR_WORKSPACE
+    assert call(P(6 * a + 4), need) == ERR_ALIGN
+    assert call(P(5 * a + 128), need) == ERR_ALIAS     # inside Y
+    assert call(P(6 * a), need, acc=P(6 * a + 4096)) == ERR_ALIAS   # acc inside the workspace
+    assert call(P(6 * a), need, Xq=None) == ERR_NULL  # the product's own checks come first
 
 
 def test_residual_forms_reject_before_launch(L):

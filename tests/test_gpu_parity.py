@@ -263,6 +263,45 @@ def test_gemm_parity(M, N, K):
     assert np.array_equal(down(y_plain).view(np.int32), o["y"].view(np.int32))
 
 
+# ------------------------------------------------------------------------------ K split (16..32 tokens, long rows)
+
+SPLIT_CASES = [
+    # (M, N, K): 8 slices of 8 K steps; 8 slices on two feature tiles; 8 slices of 14 steps on
+    # ragged token and feature tiles; 8 slices of 10 steps on a ragged feature tile; 8 slices
+    # whose last one ends inside a K step (K % 256 = 64); 8 slices of 32 steps; the 100B down
+    # projection at 32 tokens on a subset of its rows; 3 slices (many tiles)
+    (16, 96, 16384), (32, 256, 16384), (20, 200, 28672), (32, 130, 20480), (17, 50, 16448),
+    (16, 64, 65536), (32, 1024, 28672), (24, 40000, 16384),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_CASES)
+def test_split_k_parity(M, N, K):
+    """bitlinear_forward_ws (K split across blocks, int32 partials summed by a second
+    kernel): y and acc bit for bit the unsplit call's and the oracle's, also with a
+    workspace full of stale bytes reused twice; residual adds bit for bit as fp32."""
+    need = bl.bitlinear_forward_workspace_bytes(M, N, K)
+    assert need > 0, "shape must take the split path"
+    w = latents(N, K, 9900 + N + K)
+    x = make_acts(M, K, 9950 + M + K, heavy=True)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    xq, s = bl.bitlinear_quantize_act(up(x))
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+    ys, accs = bl.bitlinear_forward(xq, s, packed, gamma, acc=True, workspace=ws)
+    ys2 = bl.bitlinear_forward(xq, s, packed, gamma, workspace=ws)
+    yu, accu = bl.bitlinear_forward(xq, s, packed, gamma, acc=True, split=False)
+    o = oracle.bitlinear(x, w)
+    assert np.array_equal(down(xq), o["xq"])
+    assert np.array_equal(down(accs), o["acc"])
+    assert np.array_equal(down(accu), o["acc"])
+    for y in (ys, ys2, yu):
+        assert np.array_equal(down(y).view(np.int32), o["y"].view(np.int32))
+    y0 = datagen.outlier_acts(M, N, 9990 + M + N)
+    yr = up(y0)
+    bl.bitlinear_forward(xq, s, packed, gamma, y=yr, residual=True, workspace=ws)
+    assert np.array_equal(down(yr).view(np.int32), oracle_residual(y0, o["y"]).view(np.int32))
+
+
 # ------------------------------------------------------------------------------ residual forms
 
 RESIDUAL_CASES = [
@@ -292,7 +331,7 @@ def test_forward_f32_workspace(M, N, K, mode):
     gain, act = pro_args(mode, K, 9800 + K)
     packed, gamma = bl.bitlinear_pack_weights(up(w))
     xg, gg = up(x), None if gain is None else up(gain)
-    need = bl.bitlinear_forward_f32_workspace_bytes(M, K)
+    need = bl.bitlinear_forward_f32_workspace_bytes(M, N, K)
     assert need >= M * K + 4 * M
     ws = torch.full((need + 64,), 0x5A, dtype=torch.uint8, device=DEV)
     yw = bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, act, workspace=ws)
