@@ -10,10 +10,11 @@
 //
 // Unpack. A 16-byte chunk of a packed row holds codes k0 .. k0+63 (k0 = 64c). Dword d of
 // the chunk holds bytes 4d..4d+3, byte jj holds codes k0 + 16d + 4jj + f in bits 2f.
-// (dword >> 2f) & 0x03030303 therefore yields the four fields f of the four bytes, i.e.
-// offset codes q + 1 in {0, 1, 2} for k0 + 16d + 4jj + f, jj = 0..3. The activations are
-// held in the same order (a byte-transpose of each 16-byte group, done once per block),
-// and sum_k (q+1) x - sum_k x = sum_k q x removes the offset exactly.
+// (dword >> 2f) & 0x03030303 would yield the four fields f of the four bytes, i.e. offset
+// codes q + 1 in {0, 1, 2} for k0 + 16d + 4jj + f, jj = 0..3; the product masks them in
+// place instead (scaled by 4^f, one accumulator per scale). The activations are held in
+// the same order (a byte-transpose of each 16-byte group, done once per block), and
+// sum_k (q+1) x - sum_k x = sum_k q x removes the offset exactly.
 //
 // Work split. A row is shared by L lanes (L = 8 .. 256); lane j owns chunks j, j+L, ...
 // (at most 4/MT of them) and keeps their activation codes for MT tokens in VGPRs for
@@ -612,37 +613,46 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
             int32_t accv[R][MT];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                // independent accumulators (one per dword of a chunk for one or two tokens;
-                // with more tokens the tokens themselves are independent chains) keep the
-                // dot4 chains short; integer addition makes the split exact
-                constexpr int NP = MT >= 4 ? 1 : 4;
-                int32_t part[MT][NP];
+                // Field f of the four bytes of a dword is masked in place, not shifted down:
+                // w & 0x03030303, w & 0x0C0C0C0C and w & 0x30303030 are the offset codes of
+                // fields 0, 1, 2 times 1, 4 and 16, and (w >> 2) & 0x30303030 those of field 3
+                // times 16 (5 operations per dword instead of 7; every byte stays in 0..32, a
+                // non-negative int8). Each scale has its own accumulators, so the sum is
+                // part0 + part1 / 4 + (part2 + part3) / 16 with exact divisions (each part is
+                // a multiple of its scale; |part| <= 127 * 32 * K / 4 < 2^31 for K <= 132104).
+                // One accumulator per field for one or two tokens keeps the dot4 chains short;
+                // with more tokens the tokens themselves are independent chains and fields 2
+                // and 3 share one.
+                constexpr int NA = MT >= 4 ? 3 : 4;
+                int32_t part[MT][NA];
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
 #pragma unroll
-                    for (int d = 0; d < NP; ++d)
-                        part[t][d] = 0;
+                    for (int f = 0; f < NA; ++f)
+                        part[t][f] = 0;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
                     const uint32_t wd[4] = {w[r][i].x, w[r][i].y, w[r][i].z, w[r][i].w};
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
+                        const uint32_t u[4] = {wd[d] & 0x03030303u, wd[d] & 0x0C0C0C0Cu, wd[d] & 0x30303030u,
+                                               (wd[d] >> 2) & 0x30303030u};
 #pragma unroll
                         for (int f = 0; f < 4; ++f) {
-                            const uint32_t u = (wd[d] >> (2 * f)) & 0x03030303u;
+                            const int a = f < NA ? f : NA - 1;
 #pragma unroll
                             for (int t = 0; t < MT; ++t)
-                                part[t][d % NP] =
-                                    __builtin_amdgcn_sdot4((int)u, (int)act[t][i][4 * d + f], part[t][d % NP], false);
+                                part[t][a] = __builtin_amdgcn_sdot4((int)u[f], (int)act[t][i][4 * d + f], part[t][a], false);
                         }
                     }
                 }
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
                 {
-                    int32_t sum = part[t][0];
-                    if constexpr (NP == 4)
-                        sum = (part[t][0] + part[t][1]) + (part[t][2] + part[t][3]);
+                    int32_t hi = part[t][2];
+                    if constexpr (NA == 4)
+                        hi += part[t][3];
+                    const int32_t sum = part[t][0] + (part[t][1] >> 2) + (hi >> 4);
                     accv[r][t] = group_sum<(L < 64 ? L : 64)>(sum - xs[t]);
                 }
             }
