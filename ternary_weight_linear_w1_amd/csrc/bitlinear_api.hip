@@ -155,6 +155,8 @@ bool dispatch_mt1(const bl::FwdArgs& a, hipStream_t stream)
     if (KC <= 512) {
         if constexpr (FUSED)
             launch_k64<128, 1, 4, 1, FUSED>(a, 1, stream);
+        else if (KC <= 448)  // one wave per row (no cross-wave sum), 7 chunks per lane: 100B down
+            launch_k64<64, 1, 7, 1, FUSED>(a, 1, stream);
         else
             launch_k64<256, 1, 2, 2, FUSED>(a, 3, stream);  // codes straight to registers
         return true;

@@ -193,6 +193,9 @@ FWD_CASES = [
     # rows past 8 units re-read for their codes, every activation kind with and without norm
     (1, 33, 16384, "norm"), (1, 40, 65536, "relu2norm"), (1, 24, 65536, "gatednorm"), (1, 20, 65536, "gated"),
     (1, 40, 28672, "gated"), (1, 50, 8192, "relu2"), (1, 30, 32768, "norm"),
+    # pre-quantized rows of 257..448 chunks (one wave per row, 7 chunks per lane, some lanes
+    # holding fewer) and of 449..512 (four waves per row)
+    (1, 77, 20480, None), (1, 45, 16448, None), (1, 9, 28672, None), (1, 21, 30720, None),
 ]
 
 
