@@ -120,6 +120,9 @@ int bitlinear_quantize_act(const float* X, int64_t M, int64_t K, const float* ga
  *   Y         fp32 [M][N] (written)
  *   acc       int32 [M][N] (written) or NULL
  * A packed field equal to 3 (never written by the packer) gives unspecified results.
+ * Every token count gives the same bits: the kernel (vector dot products for a few
+ * tokens, the int8 matrix cores for 2..16 tokens on the shapes where they are faster and
+ * for 16 tokens and more) only changes the order of exact integer additions.
  */
 int bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K,
                       const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int32_t* acc,
@@ -155,16 +158,18 @@ int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const f
  * and result as bitlinear_forward_f32, or its residual form when residual != 0).
  *
  * One launch converts the input inside the product only while the tokens fit a few
- * token tiles of the decode product; from 16 tokens on, every tile would read all the
- * weights again. This entry then quantizes into the workspace and runs the matrix-core
- * product: bit for bit bitlinear_quantize_act followed by bitlinear_forward_ws (or its
- * residual form), the same result the one-launch call gives.
+ * token tiles of the decode product; from 16 tokens on every tile would read all the
+ * weights again, and from 3 tokens (2 for the largest matrices) the product is faster on
+ * the matrix cores. For those sizes this entry quantizes into the workspace and runs the
+ * matrix-core product: bit for bit bitlinear_quantize_act followed by
+ * bitlinear_forward_ws (or its residual form), the same result the one-launch call gives.
  *
  *   workspace        device scratch of at least bitlinear_forward_f32_workspace_bytes(M, N, K)
  *                    bytes, 16-byte aligned, overlapping no argument; its contents after
  *                    the call are unspecified; calls that may run concurrently need
- *                    distinct workspaces. When that size is 0 (M < 16, or sizes out of
- *                    range) the workspace is not used and may be NULL.
+ *                    distinct workspaces. When that size is 0 (one token, the sizes
+ *                    that stay on the one-launch product, or sizes out of range) the
+ *                    workspace is not used and may be NULL.
  *   residual         0: Y = product; 1: Y = fl32(Y + product)
  * Other arguments, layouts and errors as in bitlinear_forward_f32; additionally
  * BITLINEAR_ERR_NULL for a NULL workspace and BITLINEAR_ERR_WORKSPACE for a short one

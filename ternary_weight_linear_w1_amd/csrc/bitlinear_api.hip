@@ -13,6 +13,7 @@
 #include "gemm.hpp"
 #include "gemv.hpp"
 #include "gemv5.hpp"
+#include "gemv_mfma.hpp"
 #include "pack.hpp"
 #include "quant.hpp"
 
@@ -320,6 +321,40 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
     return true;
 }
 
+// Few tokens on the matrix cores (gemv_mfma_kernel, 12 waves sharing the activation codes
+// in LDS, units of 16 rows x 512 codes). Timed against the vector product and the tiled
+// matrix-core product on MI355X over the 2B and 100B shapes at 2, 4, 8 and 16 tokens: it
+// wins from 3 to 15 tokens on every shape (e.g. 100B up, 8 tokens: 17.4 against 49.9 us),
+// at 2 tokens only for the largest matrices (>= 128M weights), and at 16 tokens only for
+// matrices below 64M weights (the tiled product is faster on the larger ones).
+constexpr int kMfmaWaves = 12;
+constexpr int kMfmaUnit = 2;                   // windows of 256 codes per unit
+constexpr int64_t kMaxLds = 160 * 1024;
+
+bool mfma_small_shape(int64_t M, int64_t N, int64_t K, int64_t cus)
+{
+    if (M < 2 || M > 16 || (K % 64) != 0 || N > (int64_t(1) << 27))
+        return false;
+    const int64_t nk = N * K;
+    if ((M == 2 && nk < (int64_t(128) << 20)) || (M == 16 && nk >= (int64_t(64) << 20)))
+        return false;
+    if ((N + 16) * (K / 4) >= bl::kOob || M * K >= INT32_MAX)
+        return false;
+    const int64_t ng = (N + 15) / 16, grid = ng < cus ? ng : cus;
+    return (int64_t)bl::gemv_mfma_lds_bytes(M, K, (ng + grid - 1) / grid) <= kMaxLds;
+}
+
+bool dispatch_mfma(const bl::FwdArgs& a, hipStream_t stream)
+{
+    const int64_t cus = cu_count();
+    if (!mfma_small_shape(a.M, a.N, a.K, cus))
+        return false;
+    const int64_t ng = (a.N + 15) / 16, grid = ng < cus ? ng : cus;
+    hipLaunchKernelGGL((bl::gemv_mfma_kernel<kMfmaUnit, kMfmaWaves>), dim3((unsigned)grid), dim3(kMfmaWaves * 64),
+                       bl::gemv_mfma_lds_bytes(a.M, a.K, (ng + grid - 1) / grid), stream, a);
+    return true;
+}
+
 template <bool FUSED>
 void dispatch_forward(const bl::FwdArgs& a, bool chunk_ok, hipStream_t stream)
 {
@@ -391,7 +426,7 @@ int forward_impl(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K, c
     const int slices = splitk_slices(M, N, K);
     if (part && chunk_ok && slices > 1 && ((M + 31) / 32) * ((N + 127) / 128) * slices < INT32_MAX)
         launch_gemm_split(a, part, slices, stream);
-    else if (!(chunk_ok && dispatch_gemm(a, stream)))
+    else if (!(chunk_ok && (dispatch_mfma(a, stream) || dispatch_gemm(a, stream))))
         dispatch_forward<false>(a, chunk_ok, stream);
     return launched();
 }
@@ -426,9 +461,16 @@ int check_f32_args(const float* X, int64_t M, int64_t K, const float* gain, int 
     return BITLINEAR_OK;
 }
 
-// Token counts from which the product runs on the matrix cores (and the fused call with a
-// workspace quantizes first, then multiplies).
+// Token counts from which the product runs on the tiled matrix-core kernel.
 constexpr int64_t kGemmMinTokens = 16;
+
+// Whether the fused call with a workspace quantizes first and then multiplies: wherever the
+// product takes the matrix cores (from 16 tokens, and the few-token shapes above; the
+// size check assumes 256 CUs, the launch rechecks with the device's count).
+bool f32_two_step(int64_t M, int64_t N, int64_t K)
+{
+    return M >= kGemmMinTokens || mfma_small_shape(M, N, K, 256);
+}
 
 
 int forward_f32_impl(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
@@ -643,7 +685,7 @@ int bitlinear_forward_f32_residual(const float* X, int64_t M, int64_t K, const f
 
 size_t bitlinear_forward_f32_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    if (check_mk(M, K) != BITLINEAR_OK || M < kGemmMinTokens || check_nk(N, K) != BITLINEAR_OK || M > kMaxElems / N)
+    if (check_mk(M, K) != BITLINEAR_OK || check_nk(N, K) != BITLINEAR_OK || M > kMaxElems / N || !f32_two_step(M, N, K))
         return 0;
     return (size_t)(round256(M * K) + round256(M * 4) + split_bytes(M, N, K));
 }

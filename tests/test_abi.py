@@ -114,7 +114,9 @@ def test_forward_workspace_bytes(L):
 
 def test_forward_f32_workspace_bytes(L):
     f = bl.bitlinear_forward_f32_workspace_bytes
-    assert f(1, 96, 64) == 0 and f(15, 96, 256) == 0    # one-launch sizes need none
+    assert f(1, 96, 64) == 0 and f(2, 96, 256) == 0     # one-launch sizes need none
+    assert f(15, 96, 256) == 3840 + 256                 # 3..15 tokens: the matrix-core product
+    assert f(2, 28672, 8192) == 16384 + 256             # 2 tokens on the largest matrices
     assert f(16, 8, 256) == 4096 + 256                  # codes, then scales, each on 256 bytes
     assert f(100, 130, 260) == 26112 + 512
     assert f(2048, 6912, 6912) == 2048 * 6912 + 8192
@@ -139,8 +141,8 @@ def test_forward_f32_ws_rejects_before_launch(L):
     # the one-launch call's own checks come first
     assert call(P(6 * a), need, k=62) == ERR_SHAPE
     assert call(P(6 * a), need, X=None) == ERR_NULL
-    # below 16 tokens no workspace is needed: the one-launch checks alone apply
-    g = f(P(a), 4, K, None, 1e-5, 7, P(3 * a), P(4 * a), N, P(5 * a), 0, None, 0, None)
+    # the one-launch call's checks come before the workspace's
+    g = f(P(a), 1, K, None, 1e-5, 7, P(3 * a), P(4 * a), N, P(5 * a), 0, None, 0, None)
     assert g == ERR_SHAPE
 
 

@@ -305,6 +305,45 @@ def test_split_k_parity(M, N, K):
     assert np.array_equal(down(yr).view(np.int32), oracle_residual(y0, o["y"]).view(np.int32))
 
 
+# ------------------------------------------------------------------------------ few tokens on the matrix cores
+
+MFMA_CASES = [
+    # (M, N, K): 2..16 tokens through the matrix-core kernel with the activation codes in LDS:
+    # ragged row groups (N % 16), K past the last full window of 256 codes (K % 256 = 64, 192),
+    # one window, several row groups per block, the longest rows it takes (4 tokens at
+    # K = 28672), 16 tokens (no zero slot), 2 tokens on a matrix of >= 128M weights
+    (3, 33, 64), (4, 100, 320), (5, 257, 2560), (7, 1000, 448), (8, 130, 6912), (9, 64, 8192),
+    (12, 8200, 256), (15, 77, 1088), (16, 129, 2560), (4, 50, 28672), (2, 16400, 8192),
+]
+
+
+@pytest.mark.parametrize("M,N,K", MFMA_CASES)
+def test_mfma_small_parity(M, N, K):
+    """y and acc bit for bit the oracle's; the residual form adds in fp32 bit for bit; the
+    fused call with a workspace (quantize, then this product) equals quantize + forward."""
+    w = latents(N, K, 9500 + N + K)
+    x = make_acts(M, K, 9550 + M + K, heavy=True)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    xq, s = bl.bitlinear_quantize_act(up(x))
+    y, acc = bl.bitlinear_forward(xq, s, packed, gamma, acc=True)
+    o = oracle.bitlinear(x, w)
+    assert np.array_equal(down(xq), o["xq"])
+    assert np.array_equal(down(acc), o["acc"])
+    assert np.array_equal(down(y).view(np.int32), o["y"].view(np.int32))
+    y0 = datagen.outlier_acts(M, N, 9580 + M + N)
+    yr = up(y0)
+    bl.bitlinear_forward(xq, s, packed, gamma, y=yr, residual=True)
+    assert np.array_equal(down(yr).view(np.int32), oracle_residual(y0, o["y"]).view(np.int32))
+    gain, act = pro_args("relu2norm", K, 9590 + K)
+    xg, gg = up(x), up(gain)
+    need = bl.bitlinear_forward_f32_workspace_bytes(M, N, K)
+    ws = torch.full((max(need, 16),), 0x3C, dtype=torch.uint8, device=DEV)
+    yw = bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, act, workspace=ws)
+    xq2, s2 = bl.bitlinear_quantize_act(xg, gg, EPS, act)
+    y2 = bl.bitlinear_forward(xq2, s2, packed, gamma)
+    assert np.array_equal(down(yw).view(np.int32), down(y2).view(np.int32))
+
+
 # ------------------------------------------------------------------------------ residual forms
 
 RESIDUAL_CASES = [
@@ -321,6 +360,8 @@ WS_CASES = [
     # product), incl. ragged tiles, each input kind, and a K the matrix cores do not take
     (16, 96, 2560, None), (100, 130, 2560, "norm"), (300, 64, 6912, "relu2norm"), (64, 40, 2560, "gatednorm"),
     (33, 50, 260, "relu2"), (17, 8, 128, "gated"),
+    # few tokens through the matrix-core product
+    (4, 300, 2560, "norm"), (8, 77, 6912, "relu2norm"), (12, 130, 8192, None), (3, 50, 2560, "gatednorm"),
 ]
 
 
