@@ -329,7 +329,25 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
 // matrices below 64M weights (the tiled product is faster on the larger ones).
 constexpr int kMfmaWaves = 12;
 constexpr int kMfmaUnit = 2;                   // windows of 256 codes per unit
+constexpr int kMfmaMaxPhases = 4;              // K slices staged one after another
 constexpr int64_t kMaxLds = 160 * 1024;
+
+// Windows of 256 codes per phase of gemv_mfma_kernel (a multiple of the unit; 0: the
+// codes of one unit per window do not fit, or more than kMfmaMaxPhases phases).
+int64_t mfma_phase_windows(int64_t M, int64_t K, int64_t rg_per_block)
+{
+    const int64_t nw = (K + 255) / 256;
+    const int64_t ms = M < 16 ? M + 1 : 16;
+    int64_t maxw = (kMaxLds - (int64_t)bl::gemv_mfma_lds_bytes(M, 0, rg_per_block)) / (256 * ms);
+    maxw -= maxw % kMfmaUnit;
+    if (maxw < kMfmaUnit)
+        return 0;
+    const int64_t nph = (nw + maxw - 1) / maxw;
+    if (nph > kMfmaMaxPhases)
+        return 0;
+    const int64_t w = (nw + nph - 1) / nph;
+    return (w + kMfmaUnit - 1) / kMfmaUnit * kMfmaUnit;
+}
 
 bool mfma_small_shape(int64_t M, int64_t N, int64_t K, int64_t cus)
 {
@@ -341,7 +359,7 @@ bool mfma_small_shape(int64_t M, int64_t N, int64_t K, int64_t cus)
     if ((N + 16) * (K / 4) >= bl::kOob || M * K >= INT32_MAX)
         return false;
     const int64_t ng = (N + 15) / 16, grid = ng < cus ? ng : cus;
-    return (int64_t)bl::gemv_mfma_lds_bytes(M, K, (ng + grid - 1) / grid) <= kMaxLds;
+    return mfma_phase_windows(M, K, (ng + grid - 1) / grid) > 0;
 }
 
 bool dispatch_mfma(const bl::FwdArgs& a, hipStream_t stream)
@@ -349,9 +367,10 @@ bool dispatch_mfma(const bl::FwdArgs& a, hipStream_t stream)
     const int64_t cus = cu_count();
     if (!mfma_small_shape(a.M, a.N, a.K, cus))
         return false;
-    const int64_t ng = (a.N + 15) / 16, grid = ng < cus ? ng : cus;
+    const int64_t ng = (a.N + 15) / 16, grid = ng < cus ? ng : cus, rg = (ng + grid - 1) / grid;
+    const int64_t nwp = mfma_phase_windows(a.M, a.K, rg);
     hipLaunchKernelGGL((bl::gemv_mfma_kernel<kMfmaUnit, kMfmaWaves>), dim3((unsigned)grid), dim3(kMfmaWaves * 64),
-                       bl::gemv_mfma_lds_bytes(a.M, a.K, (ng + grid - 1) / grid), stream, a);
+                       bl::gemv_mfma_lds_bytes(a.M, nwp, rg), stream, a, (int)nwp);
     return true;
 }
 

@@ -25,6 +25,10 @@
 // 16 bytes x_i[256 w + 64 g + 4 m + f], m = 0..15 (a 16 x 4 byte transpose of the
 // 64-byte group), stored at slot ((w * 4 + g) * 4 + f) * MS + i; slot i = M (when M < 16)
 // is all zeros and serves the lanes of tokens M..15.
+//
+// Rows too long for LDS (e.g. 8 tokens at K = 28672) are walked in phases of NWP windows:
+// each phase stages its slice of the codes, runs its units, and the block synchronises
+// before the next slice overwrites it (the row sums and accumulators carry over).
 #pragma once
 
 #include "gemv.hpp"
@@ -33,16 +37,16 @@ namespace bl {
 
 typedef int mf_v4i __attribute__((ext_vector_type(4)));
 
-// LDS bytes of gemv_mfma_kernel: activation slots, the row groups' accumulators, row sums.
-inline size_t gemv_mfma_lds_bytes(int64_t M, int64_t K, int64_t rg_per_block)
+// LDS bytes of gemv_mfma_kernel with phases of nwp windows: activation slots, the row
+// groups' accumulators, row sums.
+inline size_t gemv_mfma_lds_bytes(int64_t M, int64_t nwp, int64_t rg_per_block)
 {
-    const int64_t nw = (K + 255) / 256;
     const int64_t ms = M < 16 ? M + 1 : 16;
-    return (size_t)(nw * 16 * ms * 16 + rg_per_block * 16 * 16 * 4 + 16 * 4);
+    return (size_t)(nwp * 16 * ms * 16 + rg_per_block * 16 * 16 * 4 + 16 * 4);
 }
 
 template <int WPU, int NWAVES = 8, int SI = 4>
-__global__ __launch_bounds__(NWAVES * 64) void gemv_mfma_kernel(FwdArgs a)
+__global__ __launch_bounds__(NWAVES * 64) void gemv_mfma_kernel(FwdArgs a, int nwp)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
@@ -59,11 +63,13 @@ __global__ __launch_bounds__(NWAVES * 64) void gemv_mfma_kernel(FwdArgs a)
     const int g0 = (int)((int64_t)blockIdx.x * NG / gridDim.x);
     const int g1 = (int)((int64_t)(blockIdx.x + 1) * NG / gridDim.x);
     const int RGB = g1 - g0;
-    const int KW = (NW + WPU - 1) / WPU;           // units per row group
-    const int nunits = RGB * KW;
+    const int NWP = nwp;                           // windows per phase (a multiple of WPU)
+    const int NPH = (NW + NWP - 1) / NWP;
+    const int KW = NWP / WPU;                      // units per row group and phase
+    const int nunits = RGB * KW;                   // units per phase
 
     uint8_t* As = smem;
-    int32_t* accs = reinterpret_cast<int32_t*>(smem + NW * 16 * MS * 16);
+    int32_t* accs = reinterpret_cast<int32_t*>(smem + NWP * 16 * MS * 16);
     int32_t* rsum = accs + RGB * 256;
 
     const __amdgpu_buffer_rsrc_t rw =
@@ -73,127 +79,132 @@ __global__ __launch_bounds__(NWAVES * 64) void gemv_mfma_kernel(FwdArgs a)
 
     // ---- weight loads of one unit (rows past N and windows past K read as zero)
     const int lrow = lane & 15, lg = lane >> 4;
-    auto load_unit = [&](u32x4 (&wr)[WPU], int u) {
+    auto load_unit = [&](u32x4 (&wr)[WPU], int u, int ph) {
         const bool live = u < nunits;
         const int rg = live ? u / KW : 0, p = live ? u % KW : 0;
         const int n = (g0 + rg) * 16 + lrow;
         const int base = n * KB + 16 * lg;
 #pragma unroll
         for (int s = 0; s < WPU; ++s) {
-            const int w = p * WPU + s;
+            const int w = ph * NWP + p * WPU + s;
             const int off = (live && w < NW) ? base + 64 * w : kOob;
             wr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
         }
     };
     u32x4 wr0[WPU], wr1[WPU], wr2[WPU];
-    load_unit(wr0, wave);
-    load_unit(wr1, wave + NWAVES);
-    load_unit(wr2, wave + 2 * NWAVES);
 
-    // ---- stage the activation codes (and their row sums), zero the accumulators
+    // ---- zero the accumulators, the row sums and the zero slot
     for (int i = tid; i < RGB * 256; i += NT)
         accs[i] = 0;
     if (tid < 16)
         rsum[tid] = 0;
     if (M < 16) {
-        for (int i = tid; i < NW * 16; i += NT)
+        for (int i = tid; i < NWP * 16; i += NT)
             *reinterpret_cast<uint4*>(As + (i * MS + M) * 16) = make_uint4(0u, 0u, 0u, 0u);
     }
-    __syncthreads();
-    // Every group's loads are issued before any is used (up to SI groups per thread).
-    const int items = M * NW * 4;                  // 64-byte groups (token, window, g)
-    for (int it0 = tid; it0 < items; it0 += NT * SI) {
-        u32x4 v[SI][4];
+
+    const int slot = lrow < M ? lrow : MS - 1;      // token of this lane's activation operand
+    for (int ph = 0; ph < NPH; ++ph) {
+        load_unit(wr0, wave, ph);
+        load_unit(wr1, wave + NWAVES, ph);
+        load_unit(wr2, wave + 2 * NWAVES, ph);
+        __syncthreads();                           // zeroed state, or the last phase's reads done
+
+        // ---- stage this phase's activation codes and add their row sums. Every group's
+        // loads are issued before any is used (up to SI groups per thread).
+        const int items = M * NWP * 4;             // 64-byte groups (token, window, g)
+        for (int it0 = tid; it0 < items; it0 += NT * SI) {
+            u32x4 v[SI][4];
 #pragma unroll
-        for (int k = 0; k < SI; ++k) {
-            const int it = it0 + NT * k;
-            const int t = it / (NW * 4);
-            const int k0 = 64 * (it % (NW * 4));
-            // K % 64 == 0: a group lies wholly inside or wholly past the row
-            const bool in = it < items && k0 < K;
+            for (int k = 0; k < SI; ++k) {
+                const int it = it0 + NT * k;
+                const int t = it / (NWP * 4);
+                const int k0 = 64 * (ph * NWP * 4 + it % (NWP * 4));
+                // K % 64 == 0: a group lies wholly inside or wholly past the row
+                const bool in = it < items && k0 < K;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                v[k][q] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, in ? t * K + k0 + 16 * q : kOob, 0, 0));
-        }
+                for (int q = 0; q < 4; ++q)
+                    v[k][q] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, in ? t * K + k0 + 16 * q : kOob, 0, 0));
+            }
 #pragma unroll
-        for (int k = 0; k < SI; ++k) {
-            const int it = it0 + NT * k;
-            if (it < items) {
-                const int t = it / (NW * 4);
-                const int wg = it % (NW * 4);      // window * 4 + g
-                int32_t sm = 0;
-                uint32_t o[4][4];                  // o[f][q]: bytes 4 (4q + 0..3) + f
+            for (int k = 0; k < SI; ++k) {
+                const int it = it0 + NT * k;
+                if (it < items) {
+                    const int t = it / (NWP * 4);
+                    const int wg = it % (NWP * 4);  // local window * 4 + g
+                    int32_t sm = 0;
+                    uint32_t o[4][4];               // o[f][q]: bytes 4 (4q + 0..3) + f
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sm = __builtin_amdgcn_sdot4((int)v[k][q][e], 0x01010101, sm, false);
-                    uint32_t tq[4];
-                    transpose_bytes(v[k][q][0], v[k][q][1], v[k][q][2], v[k][q][3], tq);
+                        for (int e = 0; e < 4; ++e)
+                            sm = __builtin_amdgcn_sdot4((int)v[k][q][e], 0x01010101, sm, false);
+                        uint32_t tq[4];
+                        transpose_bytes(v[k][q][0], v[k][q][1], v[k][q][2], v[k][q][3], tq);
+#pragma unroll
+                        for (int f = 0; f < 4; ++f)
+                            o[f][q] = tq[f];
+                    }
 #pragma unroll
                     for (int f = 0; f < 4; ++f)
-                        o[f][q] = tq[f];
+                        *reinterpret_cast<uint4*>(As + ((wg * 4 + f) * MS + t) * 16) =
+                            make_uint4(o[f][0], o[f][1], o[f][2], o[f][3]);
+                    atomicAdd(&rsum[t], sm);
                 }
-#pragma unroll
-                for (int f = 0; f < 4; ++f)
-                    *reinterpret_cast<uint4*>(As + ((wg * 4 + f) * MS + t) * 16) =
-                        make_uint4(o[f][0], o[f][1], o[f][2], o[f][3]);
-                atomicAdd(&rsum[t], sm);
             }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- units: 16 rows x WPU windows, products on the matrix cores
-    const int slot = lrow < M ? lrow : MS - 1;      // token of this lane's activation operand
-    auto compute_unit = [&](const u32x4 (&wr)[WPU], int u) {
-        const int rg = u / KW, p = u % KW;
-        mf_v4i c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0}, c2 = {0, 0, 0, 0}, c3 = {0, 0, 0, 0};
+        // ---- units: 16 rows x WPU windows, products on the matrix cores
+        auto compute_unit = [&](const u32x4 (&wr)[WPU], int u) {
+            const int rg = u / KW, p = u % KW;
+            mf_v4i c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0}, c2 = {0, 0, 0, 0}, c3 = {0, 0, 0, 0};
 #pragma unroll
-        for (int s = 0; s < WPU; ++s) {
-            const int w = p * WPU + s;
-            if (w < NW) {                          // uniform across the wave
-                const uint8_t* ab = As + ((w * 4 + lg) * 4 * MS + slot) * 16;
-                mf_v4i b0, b1, b2, b3;
+            for (int s = 0; s < WPU; ++s) {
+                const int lw = p * WPU + s;
+                if (ph * NWP + lw < NW) {          // uniform across the wave
+                    const uint8_t* ab = As + ((lw * 4 + lg) * 4 * MS + slot) * 16;
+                    mf_v4i b0, b1, b2, b3;
 #pragma unroll
-                for (int dd = 0; dd < 4; ++dd) {
-                    const uint32_t x = wr[s][dd];
-                    b0[dd] = (int)(x & 0x03030303u);
-                    b1[dd] = (int)(x & 0x0C0C0C0Cu);
-                    b2[dd] = (int)(x & 0x30303030u);
-                    b3[dd] = (int)((x >> 2) & 0x30303030u);
+                    for (int dd = 0; dd < 4; ++dd) {
+                        const uint32_t x = wr[s][dd];
+                        b0[dd] = (int)(x & 0x03030303u);
+                        b1[dd] = (int)(x & 0x0C0C0C0Cu);
+                        b2[dd] = (int)(x & 0x30303030u);
+                        b3[dd] = (int)((x >> 2) & 0x30303030u);
+                    }
+                    const mf_v4i a0 = *reinterpret_cast<const mf_v4i*>(ab);
+                    const mf_v4i a1 = *reinterpret_cast<const mf_v4i*>(ab + MS * 16);
+                    const mf_v4i a2 = *reinterpret_cast<const mf_v4i*>(ab + 2 * MS * 16);
+                    const mf_v4i a3 = *reinterpret_cast<const mf_v4i*>(ab + 3 * MS * 16);
+                    c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, c0, 0, 0, 0);
+                    c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, c1, 0, 0, 0);
+                    c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b2, c2, 0, 0, 0);
+                    c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, b3, c3, 0, 0, 0);
                 }
-                const mf_v4i a0 = *reinterpret_cast<const mf_v4i*>(ab);
-                const mf_v4i a1 = *reinterpret_cast<const mf_v4i*>(ab + MS * 16);
-                const mf_v4i a2 = *reinterpret_cast<const mf_v4i*>(ab + 2 * MS * 16);
-                const mf_v4i a3 = *reinterpret_cast<const mf_v4i*>(ab + 3 * MS * 16);
-                c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, c0, 0, 0, 0);
-                c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, c1, 0, 0, 0);
-                c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b2, c2, 0, 0, 0);
-                c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, b3, c3, 0, 0, 0);
             }
-        }
-        // D layout of a 16 x 16 tile: lane l, register r -> token 4 (l / 16) + r, row l % 16
+            // D layout of a 16 x 16 tile: lane l, register r -> token 4 (l / 16) + r, row l % 16
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * lg + r;
-            if (t < M)
-                atomicAdd(&accs[(rg * 16 + t) * 16 + lrow], c0[r] + (c1[r] >> 2) + ((c2[r] + c3[r]) >> 4));
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * lg + r;
+                if (t < M)
+                    atomicAdd(&accs[(rg * 16 + t) * 16 + lrow], c0[r] + (c1[r] >> 2) + ((c2[r] + c3[r]) >> 4));
+            }
+        };
+        // three named buffers in turn, so each wait for weight data sits right before its use
+        for (int u = wave; u < nunits; u += 3 * NWAVES) {
+            compute_unit(wr0, u);
+            load_unit(wr0, u + 3 * NWAVES, ph);
+            if (u + NWAVES >= nunits)
+                break;
+            compute_unit(wr1, u + NWAVES);
+            load_unit(wr1, u + 4 * NWAVES, ph);
+            if (u + 2 * NWAVES >= nunits)
+                break;
+            compute_unit(wr2, u + 2 * NWAVES);
+            load_unit(wr2, u + 5 * NWAVES, ph);
         }
-    };
-    // three named buffers in turn, so each wait for weight data sits right before its use
-    for (int u = wave; u < nunits; u += 3 * NWAVES) {
-        compute_unit(wr0, u);
-        load_unit(wr0, u + 3 * NWAVES);
-        if (u + NWAVES >= nunits)
-            break;
-        compute_unit(wr1, u + NWAVES);
-        load_unit(wr1, u + 4 * NWAVES);
-        if (u + 2 * NWAVES >= nunits)
-            break;
-        compute_unit(wr2, u + 2 * NWAVES);
-        load_unit(wr2, u + 5 * NWAVES);
     }
     __syncthreads();
 

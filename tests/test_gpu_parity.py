@@ -314,6 +314,9 @@ MFMA_CASES = [
     # K = 28672), 16 tokens (no zero slot), 2 tokens on a matrix of >= 128M weights
     (3, 33, 64), (4, 100, 320), (5, 257, 2560), (7, 1000, 448), (8, 130, 6912), (9, 64, 8192),
     (12, 8200, 256), (15, 77, 1088), (16, 129, 2560), (4, 50, 28672), (2, 16400, 8192),
+    # rows longer than LDS holds, staged in phases: 2 phases (8 tokens at K = 28672, 12 at
+    # 20480), 2 phases of 34 and 31 windows ending inside a window, 3 phases
+    (8, 100, 28672), (12, 50, 20480), (15, 33, 16448), (5, 40, 65536),
 ]
 
 
