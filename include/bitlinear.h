@@ -185,7 +185,8 @@ int bitlinear_forward_f32_ws(const float* X, int64_t M, int64_t K, const float* 
  * The product with a caller workspace (the same operation and result as bitlinear_forward,
  * or bitlinear_forward_residual when residual != 0; "BitNet b1.58 深度解析" s.2.3).
  *
- * With few tokens (16 to 32) and long rows (K >= 16384) the matrix-core product has too
+ * With few tokens (10 to 32, or 8 on matrices of >= 64M weights) and long rows
+ * (K >= 16384) the matrix-core product has too
  * few output tiles to occupy the GPU and each tile walks all of K in sequence. With a
  * workspace the K range is cut into up to 8 slices computed by separate blocks, each
  * writing its exact int32 partial sum to the workspace; a second launch adds the slices

@@ -199,8 +199,8 @@ def bitlinear_forward_workspace_bytes(M: int, N: int, K: int) -> int:
 def bitlinear_forward(Xq, x_scale, W_packed, gamma, y=None, acc=None, stream=None, residual=False,
                       workspace=None, split=True):
     """int8 activations + packed ternary weights -> fp32 y [M][N] (and int32 acc if given).
-    residual=True adds the product to the given y (no acc). With 16 to 32 tokens and long
-    rows the call goes through bitlinear_forward_ws (K split across blocks; the workspace, uint8 of at least
+    residual=True adds the product to the given y (no acc). With 10 to 32 tokens (8 on matrices of >= 64M weights) and
+    long rows the call goes through bitlinear_forward_ws (K split across blocks; the workspace, uint8 of at least
     bitlinear_forward_workspace_bytes(M, N, K), is allocated here when not given);
     split=False calls bitlinear_forward / bitlinear_forward_residual (same result)."""
     import torch

@@ -233,15 +233,20 @@ int64_t round256(int64_t b)
 constexpr int kSplitStep = 256;
 
 // K slices of the split product (1: no split). Measured on MI355X against the unsplit
-// kernel at 16..128 tokens over the 2B and 100B shapes: splitting pays only where few token
-// tiles meet a long K loop (K >= 16384: about 1.45x on the 100B down projection at 16 and
-// 32 tokens). At 64 tokens and beyond, or with shorter rows, the int32 partials (written
-// and read once more) and the second launch cost more than the shorter loop gains. Up to 8
-// slices of at least 4 K steps, aiming at about 1024 blocks; the partials are then at most
-// a quarter of the packed weight bytes (16 M s <= K / 4).
+// kernel at 16..128 tokens over the 2B and 100B shapes, and against the few-token
+// matrix-core kernel (which walks such rows in several LDS phases) at 6..15 tokens:
+// splitting pays only where few token tiles meet a long K loop (K >= 16384): from 10
+// tokens, or 8 on matrices of >= 64M weights, up to 32 (100B down projection: 35.9 ->
+// 26.5 us at 32 tokens, 30.8 -> 22.7 at 12). At 64 tokens and beyond, or with shorter
+// rows, the int32 partials (written and read once more) and the second launch cost more
+// than the shorter loop gains. Up to 8 slices of at least 4 K steps, aiming at about 1024
+// blocks; the partials are then at most a quarter of the packed weight bytes
+// (16 M s <= K / 4).
 int splitk_slices(int64_t M, int64_t N, int64_t K)
 {
-    if (M < 16 || M > 32 || (K % 64) != 0 || K < 16384)
+    if (M < 8 || M > 32 || (K % 64) != 0 || K < 16384)
+        return 1;
+    if (M < 10 && N * K < (int64_t(64) << 20))
         return 1;
     const int64_t tiles = ((M + 31) / 32) * ((N + 127) / 128);
     const int64_t nk = (K + kSplitStep - 1) / kSplitStep;

@@ -99,7 +99,7 @@ def test_forward_f32_rejects_before_launch(L):
 
 def test_forward_workspace_bytes(L):
     f = bl.bitlinear_forward_workspace_bytes
-    # K split for 16..32 tokens and K >= 16384: up to 8 slices of >= 4 K steps of 256,
+    # K split for 10..32 tokens (8 on >= 64M weights) and K >= 16384: up to 8 slices of >= 4 K steps of 256,
     # about 1024 blocks; slices x M x N int32 partials
     assert f(16, 8192, 28672) == 8 * 16 * 8192 * 4      # 64 tiles of 32 x 128: capped at 8
     assert f(32, 8192, 28672) == 8 * 32 * 8192 * 4
@@ -107,7 +107,10 @@ def test_forward_workspace_bytes(L):
     assert f(32, 20000, 16384) == 6 * 32 * 20000 * 4    # 157 tiles: 6 slices
     assert f(20, 64, 16384) == 8 * 20 * 64 * 4          # 64 K steps: 16 of 4, capped at 8
     assert f(16, 96, 2560) == 0 and f(32, 10240, 8192) == 0            # short rows: no split
-    assert f(15, 8192, 28672) == 0 and f(33, 8192, 28672) == 0         # token range
+    assert f(7, 8192, 28672) == 0 and f(33, 8192, 28672) == 0          # token range
+    assert f(8, 8192, 28672) == 8 * 8 * 8192 * 4        # 8 tokens on >= 64M weights
+    assert f(8, 2560, 16384) == 0                       # ... not on smaller matrices
+    assert f(12, 2560, 16384) == 8 * 12 * 2560 * 4      # from 10 tokens on any
     assert f(16, 128, 16400) == 0                       # K % 64
     assert f(0, 64, 64) == 0 and f(16, 64, 62) == 0                    # out of range
 

@@ -266,7 +266,7 @@ def test_gemm_parity(M, N, K):
     assert np.array_equal(down(y_plain).view(np.int32), o["y"].view(np.int32))
 
 
-# ------------------------------------------------------------------------------ K split (16..32 tokens, long rows)
+# ------------------------------------------------------------------------------ K split (10..32 tokens, long rows)
 
 SPLIT_CASES = [
     # (M, N, K): 8 slices of 8 K steps; 8 slices on two feature tiles; 8 slices of 14 steps on
@@ -275,6 +275,8 @@ SPLIT_CASES = [
     # projection at 32 tokens on a subset of its rows; 3 slices (many tiles)
     (16, 96, 16384), (32, 256, 16384), (20, 200, 28672), (32, 130, 20480), (17, 50, 16448),
     (16, 64, 65536), (32, 1024, 28672), (24, 40000, 16384),
+    # from 10 tokens (and 8 on matrices of >= 64M weights): one token tile of few rows
+    (10, 64, 16384), (13, 130, 20480), (8, 4100, 16384),
 ]
 
 
