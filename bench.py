@@ -303,6 +303,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary configurations")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only the decode-attention cases (a short program for kernel traces)")
+    ap.add_argument("--few-tokens-only", action="store_true",
+                    help="time only the 4- and 8-token products (a short program for kernel traces)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the M = 2048 prefill products (a short program for counter passes)")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_CSV", "OUT"),
@@ -348,6 +350,9 @@ def main():
         return 0
     if args.prefill_only:
         print(json.dumps({"2B_prefill_M2048": run_prefill(torch, bl, datagen, dev, 2048)}))
+        return 0
+    if args.few_tokens_only:
+        print(json.dumps(run_few(torch, bl, datagen, dev)))
         return 0
 
     # ---- the 2B layer at M = 1
@@ -513,13 +518,11 @@ def run_peaks(torch, dev):
     return out
 
 
-def run_extra(torch, bl, datagen, dev, mats2b):
+def run_few(torch, bl, datagen, dev):
+    """A few tokens: the 2B layer at M = 4 and 8 (fused call, product on pre-quantized codes,
+    quantization launch alone) and the 100B slice's product at M = 8, weights rotating
+    through HBM as at M = 1."""
     res = {}
-    res["cfg1_single_M1"] = run_cfg1(torch, bl, datagen, dev)
-    res["measured_peaks"] = run_peaks(torch, dev)
-    torch.cuda.empty_cache()
-    # ---- 2B layer at M = 4, 8: the fused call, the product on pre-quantized codes and the
-    # quantization launch on its own (weights rotating as at M = 1)
     for M in (4, 8):
         r = {}
         for i, (name, N, K, mode) in enumerate(LAYER_2B):
@@ -537,6 +540,32 @@ def run_extra(torch, bl, datagen, dev, mats2b):
             torch.cuda.empty_cache()
         res["2B_M%d" % M] = r
         log("extra 2B M=%d: %s" % (M, r))
+    M, r = 8, {}
+    for i, (name, N, K, mode) in enumerate(LAYER_100B):
+        C = n_copies(N * K // 4)
+        m = Mat(torch, bl, datagen, 5, 8 + i, name, N, K, mode, M, C, dev)
+        m.prequant(bl)
+        need = bl.bitlinear_forward_workspace_bytes(M, N, K)
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        a = time_kernel(torch, lambda c, m=m: m.forward(bl, c, ws), C, 100)
+        b = m.bytes(fused=False)
+        r[name] = {"us": round(a * 1e6, 2), "GB/s": round(b / a / 1e9, 1),
+                   "frac_hbm": round(b / a / 1e9 / HBM_PEAK_GBS, 4)}
+        if need:
+            r[name]["k_slices"] = need // (4 * M * N)
+        del m, ws
+        torch.cuda.empty_cache()
+    res["100B_M8"] = r
+    log("extra 100B M=8: %s" % r)
+    return res
+
+
+def run_extra(torch, bl, datagen, dev, mats2b):
+    res = {}
+    res["cfg1_single_M1"] = run_cfg1(torch, bl, datagen, dev)
+    res["measured_peaks"] = run_peaks(torch, dev)
+    torch.cuda.empty_cache()
+    res.update(run_few(torch, bl, datagen, dev))
     torch.cuda.empty_cache()
     # ---- 100B-shaped slice at M = 1 (fused), M = 32 and 64 (pre-quantized; at 32 tokens the
     #      down projection's K is split across blocks, timed beside the unsplit product)
