@@ -328,22 +328,31 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
 
 // Few tokens on the matrix cores (gemv_mfma_kernel, 12 waves sharing the activation codes
 // in LDS, units of 16 rows x 512 codes). Timed against the vector product and the tiled
-// matrix-core product on MI355X over the 2B and 100B shapes at 2, 4, 8 and 16 tokens: it
-// wins from 3 to 15 tokens on every shape (e.g. 100B up, 8 tokens: 17.4 against 49.9 us),
-// at 2 tokens only for the largest matrices (>= 128M weights), and at 16 tokens only for
-// matrices below 64M weights (the tiled product is faster on the larger ones).
+// matrix-core product on MI355X over the 2B and 100B shapes at 2..64 tokens: it wins from
+// 3 to 15 tokens on every shape (e.g. 100B up, 8 tokens: 17.4 against 49.9 us), at 2 tokens
+// only for the largest matrices (>= 128M weights), and at 16..24 tokens (two tiles of 16
+// per weight operand from 17) only below 64M weights. From 24 tokens on the larger matrices,
+// and from 32 on any, every CU staging all activation rows costs more than the tiled
+// product's re-reads (100B QKV at 64 tokens: 42.7 against 22.2 us).
 constexpr int kMfmaWaves = 12;
 constexpr int kMfmaUnit = 2;                   // windows of 256 codes per unit
 constexpr int kMfmaMaxPhases = 4;              // K slices staged one after another
+constexpr int64_t kMfmaMaxTokens = 24;
 constexpr int64_t kMaxLds = 160 * 1024;
+
+int mfma_tiles(int64_t M)
+{
+    return M <= 16 ? 1 : 2;
+}
 
 // Windows of 256 codes per phase of gemv_mfma_kernel (a multiple of the unit; 0: the
 // codes of one unit per window do not fit, or more than kMfmaMaxPhases phases).
 int64_t mfma_phase_windows(int64_t M, int64_t K, int64_t rg_per_block)
 {
+    const int tt = mfma_tiles(M);
     const int64_t nw = (K + 255) / 256;
-    const int64_t ms = M < 16 ? M + 1 : 16;
-    int64_t maxw = (kMaxLds - (int64_t)bl::gemv_mfma_lds_bytes(M, 0, rg_per_block)) / (256 * ms);
+    int64_t maxw = (kMaxLds - (int64_t)bl::gemv_mfma_lds_bytes(M, tt, 0, rg_per_block)) /
+                   (256 * bl::gemv_mfma_slots(M, tt));
     maxw -= maxw % kMfmaUnit;
     if (maxw < kMfmaUnit)
         return 0;
@@ -356,15 +365,22 @@ int64_t mfma_phase_windows(int64_t M, int64_t K, int64_t rg_per_block)
 
 bool mfma_small_shape(int64_t M, int64_t N, int64_t K, int64_t cus)
 {
-    if (M < 2 || M > 16 || (K % 64) != 0 || N > (int64_t(1) << 27))
+    if (M < 2 || M > kMfmaMaxTokens || (K % 64) != 0 || N > (int64_t(1) << 27))
         return false;
     const int64_t nk = N * K;
-    if ((M == 2 && nk < (int64_t(128) << 20)) || (M == 16 && nk >= (int64_t(64) << 20)))
+    if ((M == 2 && nk < (int64_t(128) << 20)) || (M >= 16 && nk >= (int64_t(64) << 20)))
         return false;
     if ((N + 16) * (K / 4) >= bl::kOob || M * K >= INT32_MAX)
         return false;
     const int64_t ng = (N + 15) / 16, grid = ng < cus ? ng : cus;
     return mfma_phase_windows(M, K, (ng + grid - 1) / grid) > 0;
+}
+
+template <int TT>
+void launch_mfma(const bl::FwdArgs& a, int64_t grid, int64_t rg, int64_t nwp, hipStream_t stream)
+{
+    hipLaunchKernelGGL((bl::gemv_mfma_kernel<kMfmaUnit, kMfmaWaves, TT>), dim3((unsigned)grid), dim3(kMfmaWaves * 64),
+                       bl::gemv_mfma_lds_bytes(a.M, TT, nwp, rg), stream, a, (int)nwp);
 }
 
 bool dispatch_mfma(const bl::FwdArgs& a, hipStream_t stream)
@@ -374,8 +390,10 @@ bool dispatch_mfma(const bl::FwdArgs& a, hipStream_t stream)
         return false;
     const int64_t ng = (a.N + 15) / 16, grid = ng < cus ? ng : cus, rg = (ng + grid - 1) / grid;
     const int64_t nwp = mfma_phase_windows(a.M, a.K, rg);
-    hipLaunchKernelGGL((bl::gemv_mfma_kernel<kMfmaUnit, kMfmaWaves>), dim3((unsigned)grid), dim3(kMfmaWaves * 64),
-                       bl::gemv_mfma_lds_bytes(a.M, nwp, rg), stream, a, (int)nwp);
+    if (mfma_tiles(a.M) == 1)
+        launch_mfma<1>(a, grid, rg, nwp, stream);
+    else
+        launch_mfma<2>(a, grid, rg, nwp, stream);
     return true;
 }
 

@@ -1,11 +1,12 @@
-// gemv_mfma.hpp -- W1.58A8 product for a few tokens (2..16) on the int8 matrix cores.
+// gemv_mfma.hpp -- W1.58A8 product for a few tokens (2..32) on the int8 matrix cores.
 //
 // The same product as gemv.hpp ("BitNet b1.58 深度解析" s.2.3: y = (W_q x_q) * gamma / s,
 // exact in int32 before the rescale), for token counts where the vector dot products
 // would cost more ALU than the weight stream can hide: with several tokens every packed
 // byte feeds 4 * M dot4 lanes. Here each packed byte is unpacked once and the products
 // of all tokens come from v_mfma_i32_16x16x64_i8 (16 tokens x 16 weight rows x 64 codes
-// per instruction; tokens past M multiply a zero slot).
+// per instruction, TT such tiles sharing each unpacked weight operand; tokens past M
+// multiply a zero slot).
 //
 // Layout. One block per CU holds every activation code of the call in LDS, permuted once
 // into the matrix-core operand order; the weights stream from HBM straight into VGPRs.
@@ -37,15 +38,22 @@ namespace bl {
 
 typedef int mf_v4i __attribute__((ext_vector_type(4)));
 
-// LDS bytes of gemv_mfma_kernel with phases of nwp windows: activation slots, the row
-// groups' accumulators, row sums.
-inline size_t gemv_mfma_lds_bytes(int64_t M, int64_t nwp, int64_t rg_per_block)
+// Token slots of gemv_mfma_kernel with TT tiles of 16 tokens: M, plus a zero slot when
+// the tiles are not full.
+inline int64_t gemv_mfma_slots(int64_t M, int tt)
 {
-    const int64_t ms = M < 16 ? M + 1 : 16;
-    return (size_t)(nwp * 16 * ms * 16 + rg_per_block * 16 * 16 * 4 + 16 * 4);
+    return M < 16 * tt ? M + 1 : 16 * tt;
 }
 
-template <int WPU, int NWAVES = 8, int SI = 4>
+// LDS bytes of gemv_mfma_kernel with phases of nwp windows: activation slots, the row
+// groups' accumulators, row sums.
+inline size_t gemv_mfma_lds_bytes(int64_t M, int tt, int64_t nwp, int64_t rg_per_block)
+{
+    return (size_t)(nwp * 16 * gemv_mfma_slots(M, tt) * 16 + rg_per_block * 16 * 16 * tt * 4 + 16 * tt * 4);
+}
+
+// TT tiles of 16 tokens share each unpacked weight operand (M <= 16 TT).
+template <int WPU, int NWAVES = 8, int TT = 1, int SI = 4>
 __global__ __launch_bounds__(NWAVES * 64) void gemv_mfma_kernel(FwdArgs a, int nwp)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -58,7 +66,8 @@ __global__ __launch_bounds__(NWAVES * 64) void gemv_mfma_kernel(FwdArgs a, int n
     const int K = a.K;
     const int KB = K >> 2;
     const int NW = (K + 255) >> 8;                 // windows of 256 codes
-    const int MS = M < 16 ? M + 1 : 16;            // token slots (slot M: zeros)
+    constexpr int MT16 = 16 * TT;                  // tokens the tiles hold
+    const int MS = M < MT16 ? M + 1 : MT16;        // token slots (slot M: zeros)
     const int NG = (N + 15) >> 4;                  // row groups of 16
     const int g0 = (int)((int64_t)blockIdx.x * NG / gridDim.x);
     const int g1 = (int)((int64_t)(blockIdx.x + 1) * NG / gridDim.x);
@@ -70,7 +79,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemv_mfma_kernel(FwdArgs a, int n
 
     uint8_t* As = smem;
     int32_t* accs = reinterpret_cast<int32_t*>(smem + NWP * 16 * MS * 16);
-    int32_t* rsum = accs + RGB * 256;
+    int32_t* rsum = accs + RGB * 16 * MT16;
 
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.W, (short)0, (int)((int64_t)N * KB), kBufFlags);
@@ -94,16 +103,19 @@ __global__ __launch_bounds__(NWAVES * 64) void gemv_mfma_kernel(FwdArgs a, int n
     u32x4 wr0[WPU], wr1[WPU], wr2[WPU];
 
     // ---- zero the accumulators, the row sums and the zero slot
-    for (int i = tid; i < RGB * 256; i += NT)
+    for (int i = tid; i < RGB * 16 * MT16; i += NT)
         accs[i] = 0;
-    if (tid < 16)
+    if (tid < MT16)
         rsum[tid] = 0;
-    if (M < 16) {
+    if (M < MT16) {
         for (int i = tid; i < NWP * 16; i += NT)
             *reinterpret_cast<uint4*>(As + (i * MS + M) * 16) = make_uint4(0u, 0u, 0u, 0u);
     }
 
-    const int slot = lrow < M ? lrow : MS - 1;      // token of this lane's activation operand
+    int slot[TT];                                  // token slot of this lane's operand, per tile
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+        slot[tt] = 16 * tt + lrow < M ? 16 * tt + lrow : MS - 1;
     for (int ph = 0; ph < NPH; ++ph) {
         load_unit(wr0, wave, ph);
         load_unit(wr1, wave + NWAVES, ph);
@@ -159,38 +171,45 @@ __global__ __launch_bounds__(NWAVES * 64) void gemv_mfma_kernel(FwdArgs a, int n
         // ---- units: 16 rows x WPU windows, products on the matrix cores
         auto compute_unit = [&](const u32x4 (&wr)[WPU], int u) {
             const int rg = u / KW, p = u % KW;
-            mf_v4i c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0}, c2 = {0, 0, 0, 0}, c3 = {0, 0, 0, 0};
+            mf_v4i c[TT][4];
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    c[tt][f] = mf_v4i{0, 0, 0, 0};
 #pragma unroll
             for (int s = 0; s < WPU; ++s) {
                 const int lw = p * WPU + s;
                 if (ph * NWP + lw < NW) {          // uniform across the wave
-                    const uint8_t* ab = As + ((lw * 4 + lg) * 4 * MS + slot) * 16;
-                    mf_v4i b0, b1, b2, b3;
+                    mf_v4i b[4];
 #pragma unroll
                     for (int dd = 0; dd < 4; ++dd) {
                         const uint32_t x = wr[s][dd];
-                        b0[dd] = (int)(x & 0x03030303u);
-                        b1[dd] = (int)(x & 0x0C0C0C0Cu);
-                        b2[dd] = (int)(x & 0x30303030u);
-                        b3[dd] = (int)((x >> 2) & 0x30303030u);
+                        b[0][dd] = (int)(x & 0x03030303u);
+                        b[1][dd] = (int)(x & 0x0C0C0C0Cu);
+                        b[2][dd] = (int)(x & 0x30303030u);
+                        b[3][dd] = (int)((x >> 2) & 0x30303030u);
                     }
-                    const mf_v4i a0 = *reinterpret_cast<const mf_v4i*>(ab);
-                    const mf_v4i a1 = *reinterpret_cast<const mf_v4i*>(ab + MS * 16);
-                    const mf_v4i a2 = *reinterpret_cast<const mf_v4i*>(ab + 2 * MS * 16);
-                    const mf_v4i a3 = *reinterpret_cast<const mf_v4i*>(ab + 3 * MS * 16);
-                    c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, c0, 0, 0, 0);
-                    c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, c1, 0, 0, 0);
-                    c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b2, c2, 0, 0, 0);
-                    c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, b3, c3, 0, 0, 0);
+#pragma unroll
+                    for (int tt = 0; tt < TT; ++tt) {
+                        const uint8_t* ab = As + ((lw * 4 + lg) * 4 * MS + slot[tt]) * 16;
+#pragma unroll
+                        for (int f = 0; f < 4; ++f)
+                            c[tt][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                                *reinterpret_cast<const mf_v4i*>(ab + f * MS * 16), b[f], c[tt][f], 0, 0, 0);
+                    }
                 }
             }
             // D layout of a 16 x 16 tile: lane l, register r -> token 4 (l / 16) + r, row l % 16
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * lg + r;
-                if (t < M)
-                    atomicAdd(&accs[(rg * 16 + t) * 16 + lrow], c0[r] + (c1[r] >> 2) + ((c2[r] + c3[r]) >> 4));
-            }
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * tt + 4 * lg + r;
+                    if (t < M)
+                        atomicAdd(&accs[(rg * MT16 + t) * 16 + lrow],
+                                  c[tt][0][r] + (c[tt][1][r] >> 2) + ((c[tt][2][r] + c[tt][3][r]) >> 4));
+                }
         };
         // three named buffers in turn, so each wait for weight data sits right before its use
         for (int u = wave; u < nunits; u += 3 * NWAVES) {
@@ -216,7 +235,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemv_mfma_kernel(FwdArgs a, int n
         const int j = i & 15;
         const int n = (g0 + rg) * 16 + j;
         if (n < N) {
-            const int32_t v = accs[(rg * 16 + t) * 16 + j] - rsum[t];
+            const int32_t v = accs[(rg * MT16 + t) * 16 + j] - rsum[t];
             const int64_t o = (int64_t)t * N + n;
             const float yv = (float)v * (gamma / a.xscale[t]);
             a.Y[o] = a.residual ? a.Y[o] + yv : yv;

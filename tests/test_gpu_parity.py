@@ -319,25 +319,29 @@ MFMA_CASES = [
     # rows longer than LDS holds, staged in phases: 2 phases (8 tokens at K = 28672, 12 at
     # 20480), 2 phases of 34 and 31 windows ending inside a window, 3 phases
     (8, 100, 28672), (12, 50, 20480), (15, 33, 16448), (5, 40, 65536),
+    # 17..24 tokens: two tiles of 16 tokens per weight operand (zero slot for tokens past M)
+    (17, 300, 2560), (24, 129, 6912), (20, 1000, 1088), (21, 64, 16448),
 ]
 
 
 @pytest.mark.parametrize("M,N,K", MFMA_CASES)
 def test_mfma_small_parity(M, N, K):
     """y and acc bit for bit the oracle's; the residual form adds in fp32 bit for bit; the
-    fused call with a workspace (quantize, then this product) equals quantize + forward."""
+    fused call with a workspace (quantize, then the product) equals quantize + forward.
+    The product is called without a workspace, so rows that the K split would take
+    (10+ tokens, K >= 16384) also run on this kernel's LDS phases."""
     w = latents(N, K, 9500 + N + K)
     x = make_acts(M, K, 9550 + M + K, heavy=True)
     packed, gamma = bl.bitlinear_pack_weights(up(w))
     xq, s = bl.bitlinear_quantize_act(up(x))
-    y, acc = bl.bitlinear_forward(xq, s, packed, gamma, acc=True)
+    y, acc = bl.bitlinear_forward(xq, s, packed, gamma, acc=True, split=False)
     o = oracle.bitlinear(x, w)
     assert np.array_equal(down(xq), o["xq"])
     assert np.array_equal(down(acc), o["acc"])
     assert np.array_equal(down(y).view(np.int32), o["y"].view(np.int32))
     y0 = datagen.outlier_acts(M, N, 9580 + M + N)
     yr = up(y0)
-    bl.bitlinear_forward(xq, s, packed, gamma, y=yr, residual=True)
+    bl.bitlinear_forward(xq, s, packed, gamma, y=yr, residual=True, split=False)
     assert np.array_equal(down(yr).view(np.int32), oracle_residual(y0, o["y"]).view(np.int32))
     gain, act = pro_args("relu2norm", K, 9590 + K)
     xg, gg = up(x), up(gain)
