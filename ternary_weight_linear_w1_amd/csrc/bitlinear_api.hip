@@ -326,7 +326,7 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
     return true;
 }
 
-// Few tokens on the matrix cores (gemv_mfma_kernel, 12 waves sharing the activation codes
+// Few tokens on the matrix cores (gemv_mfma_kernel, 16 waves sharing the activation codes
 // in LDS, units of 16 rows x 512 codes). Timed against the vector product and the tiled
 // matrix-core product on MI355X over the 2B and 100B shapes at 2..64 tokens: it wins from
 // 3 to 15 tokens on every shape (e.g. 100B up, 8 tokens: 17.4 against 49.9 us), at 2 tokens
@@ -334,7 +334,7 @@ bool dispatch_gemm(const bl::FwdArgs& a, hipStream_t stream)
 // per weight operand from 17) only below 64M weights. From 24 tokens on the larger matrices,
 // and from 32 on any, every CU staging all activation rows costs more than the tiled
 // product's re-reads (100B QKV at 64 tokens: 42.7 against 22.2 us).
-constexpr int kMfmaWaves = 12;
+constexpr int kMfmaWaves = 16;
 constexpr int kMfmaUnit = 2;                   // windows of 256 codes per unit
 constexpr int kMfmaMaxPhases = 4;              // K slices staged one after another
 constexpr int64_t kMfmaMaxTokens = 24;
