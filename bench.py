@@ -56,6 +56,12 @@ LAYER_2B = [("qkv", 3840, 2560, "plain"), ("o", 2560, 2560, "norm"), ("up", 6912
 LAYER_100B = [("qkv", 10240, 8192, "plain"), ("o", 8192, 8192, "norm"), ("up", 28672, 8192, "plain"),
               ("down", 8192, 28672, "relu2norm")]
 
+# One GPU's share of the 100B slice under an 8-way tensor-parallel split (design only; the
+# collectives are not part of this build): QKV and up split along N (no exchange), O and
+# down along K (an exact int32 all-reduce of the partial products would follow).
+LAYER_100B_TP8 = [("qkv", 1280, 8192, "plain"), ("o", 8192, 1024, "norm"), ("up", 3584, 8192, "plain"),
+                  ("down", 8192, 3584, "relu2norm")]
+
 DOMINANT = "down"
 # What decides the measured GEMV's traffic: its kernel, the shared device helpers, and the
 # GEMV launch-shape section of the API file (from its "forward dispatch" banner to the MFMA
@@ -303,6 +309,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary configurations")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only the decode-attention cases (a short program for kernel traces)")
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="time only the calibration kernels and the vendor GEMM")
     ap.add_argument("--few-tokens-only", action="store_true",
                     help="time only the 4- and 8-token products (a short program for kernel traces)")
     ap.add_argument("--prefill-only", action="store_true",
@@ -350,6 +358,9 @@ def main():
         return 0
     if args.prefill_only:
         print(json.dumps({"2B_prefill_M2048": run_prefill(torch, bl, datagen, dev, 2048)}))
+        return 0
+    if args.peaks_only:
+        print(json.dumps(run_peaks(torch, dev)))
         return 0
     if args.few_tokens_only:
         print(json.dumps(run_few(torch, bl, datagen, dev)))
@@ -489,17 +500,55 @@ def run_cfg1(torch, bl, datagen, dev):
 
 
 def run_peaks(torch, dev):
-    """Achievable peaks on this GPU, for context next to the specs: a streaming read (torch
-    sum over 1 GiB of fp32), a streaming copy (1 GiB read + 1 GiB written), and the vendor
-    int8 GEMM (torch._int_mm, int8 x int8 -> int32, hipBLASLt on ROCm) on the 2B prefill
-    shapes at M = 2048 (dense int8 weights: 4x the bytes of the packed ternary ones)."""
+    """Achievable peaks on this GPU, for context next to the specs: a streaming-read kernel
+    (libbitlinear_peaks.so; back-to-back launches in a graph over rotating copies, best of
+    grid sizes and loads in flight) at the packed sizes of the 2B and 100B matrices, a pure
+    int8 matrix-core instruction loop, a streaming copy (torch), and the vendor int8 GEMM
+    (torch._int_mm, int8 x int8 -> int32, hipBLASLt on ROCm) on the 2B prefill shapes at
+    M = 2048 (dense int8 weights: 4x the bytes of the packed ternary ones)."""
+    import ctypes
+    from ternary_weight_linear_w1_amd import _build
+    if not os.path.exists(_build.PEAKS_LIB):
+        _build.build()
+    P = ctypes.CDLL(_build.PEAKS_LIB)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    P.bl_peak_stream_read.argtypes = [vp, i64, ci, ci, vp, vp]
+    P.bl_peak_mfma_i8.argtypes = [ci, ci, vp, vp]
     out = {}
+    sink = torch.zeros((4096 * 256,), dtype=torch.int32, device=dev)
+
+    def cur():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    reads = {}
+    for name, nbytes in (("2B up/down 4.42 MB", 4423680), ("100B O 16.78 MB", 16777216),
+                         ("100B QKV 20.97 MB", 20971520), ("100B up/down 58.72 MB", 58720256)):
+        copies = max(2, min(64, (1200 << 20) // nbytes))
+        buf = torch.empty((copies * nbytes,), dtype=torch.uint8, device=dev)
+        base = buf.data_ptr()
+        best = None
+        for blocks in (256, 512, 1024, 2048):
+            for unroll in (4, 8):
+                t = time_kernel(torch, lambda c, b=blocks, u=unroll: P.bl_peak_stream_read(
+                    ctypes.c_void_p(base + c * nbytes), nbytes, b, u, ctypes.c_void_p(sink.data_ptr()), cur()),
+                    copies, 40)
+                if best is None or t < best[0]:
+                    best = (t, blocks, unroll)
+        reads[name] = {"us": round(best[0] * 1e6, 2), "GB/s": round(nbytes / best[0] / 1e9, 1),
+                       "frac_hbm": round(nbytes / best[0] / 1e9 / HBM_PEAK_GBS, 4),
+                       "blocks": best[1], "loads_in_flight": best[2]}
+        del buf
+        torch.cuda.empty_cache()
+    out["stream_read (per launch, back to back)"] = reads
+    blocks, iters = 2 * 256, 4000
+    t = time_kernel(torch, lambda c: P.bl_peak_mfma_i8(iters, blocks, ctypes.c_void_p(sink.data_ptr()), cur()), 1, 5)
+    ops = blocks * 4 * iters * 4 * 65536.0
+    out["mfma_i8_loop"] = {"POPS": round(ops / t / 1e15, 3), "frac_int8_peak": round(ops / t / 1e15 / 5.0, 4),
+                           "us": round(t * 1e6, 1)}
     x = torch.ones((1 << 28,), dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
-    t = time_kernel(torch, lambda c: x.sum(), 1, 10)
-    out["stream_read_GB/s"] = round(x.numel() * 4 / t / 1e9, 1)
     t = time_kernel(torch, lambda c: y.copy_(x), 1, 10)
-    out["stream_copy_GB/s (read + write)"] = round(2 * x.numel() * 4 / t / 1e9, 1)
+    out["stream_copy_GB/s (read + write, torch)"] = round(2 * x.numel() * 4 / t / 1e9, 1)
     del x, y
     torch.cuda.empty_cache()
     gemm = {}
@@ -516,6 +565,26 @@ def run_peaks(torch, dev):
     out["torch_int_mm_M2048"] = gemm
     log("extra measured peaks: %s" % out)
     return out
+
+
+def run_tp8(torch, bl, datagen, dev):
+    """The 100B slice at M = 1 on one GPU's share of an 8-way tensor-parallel split: the
+    fused call and the product on pre-quantized codes (weights rotating through HBM)."""
+    r = {}
+    for i, (name, N, K, mode) in enumerate(LAYER_100B_TP8):
+        C = n_copies(N * K // 4)
+        m = Mat(torch, bl, datagen, 6, i, name, N, K, mode, 1, C, dev)
+        a = time_kernel(torch, lambda c, m=m: m.fused(bl, c), C, 100)
+        b = m.bytes()
+        m.prequant(bl)
+        f = time_kernel(torch, lambda c, m=m: m.forward(bl, c), C, 100)
+        fb = m.bytes(fused=False)
+        r[name] = {"N": N, "K": K, "fused_us": round(a * 1e6, 2), "fused_GB/s": round(b / a / 1e9, 1),
+                   "forward_us": round(f * 1e6, 2), "forward_GB/s": round(fb / f / 1e9, 1)}
+        del m
+        torch.cuda.empty_cache()
+    log("extra 100B TP8 shard M=1: %s" % r)
+    return r
 
 
 def run_few(torch, bl, datagen, dev):
@@ -603,6 +672,8 @@ def run_extra(torch, bl, datagen, dev, mats2b):
             torch.cuda.empty_cache()
         res["100B_M%d" % M] = r
         log("extra 100B M=%d: %s" % (M, r))
+    # ---- one GPU's share of the 100B slice under 8-way tensor parallelism, M = 1
+    res["100B_TP8_shard_M1"] = run_tp8(torch, bl, datagen, dev)
     # ---- prefill on the 2B shapes (pre-quantized forward), int8 TOPS
     for M in (512, 2048):
         res["2B_prefill_M%d" % M] = run_prefill(torch, bl, datagen, dev, M)

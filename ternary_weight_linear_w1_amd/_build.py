@@ -1,4 +1,5 @@
-"""Compile the HIP sources into ``libbitlinear.so`` (in-tree) with hipcc for gfx950."""
+"""Compile the HIP sources into ``libbitlinear.so`` (in-tree) with hipcc for gfx950, and the
+benchmark's calibration kernels into ``libbitlinear_peaks.so``."""
 from __future__ import annotations
 
 import os
@@ -10,6 +11,8 @@ LIB = os.path.join(HERE, "libbitlinear.so")
 SOURCES = [os.path.join(CSRC, "bitlinear_api.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")] + [
     os.path.join(os.path.dirname(HERE), "include", "bitlinear.h")]
+PEAKS_LIB = os.path.join(HERE, "libbitlinear_peaks.so")
+PEAKS_SOURCES = [os.path.join(CSRC, "peaks.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -29,15 +32,20 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def _compile(sources, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *sources, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
     if verbose and r.stderr:
         print(r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(SOURCES, LIB, verbose)
+    _compile(PEAKS_SOURCES, PEAKS_LIB, verbose)
     return LIB
 
 
