@@ -460,3 +460,50 @@ def test_binding_rejects_short_buffers():
     with pytest.raises(ValueError):
         bl.bitlinear_forward(xq, s, packed, gamma, y=torch.empty((3, 40), dtype=torch.float32, device=DEV),
                              residual=True, acc=True)
+
+
+# ------------------------------------------------------------------------------ graph replay
+
+@pytest.mark.parametrize("M,N,K,mode", [
+    (1, 300, 2560, "relu2norm"),     # one-token fused product
+    (8, 500, 2560, None),            # few tokens on the matrix cores
+    (12, 200, 16384, None),          # K split across blocks (workspace, reduce kernel)
+    (40, 300, 2560, None),           # tiled matrix-core product
+])
+def test_products_graph_replay(M, N, K, mode):
+    """A captured graph of the product (with its workspace where it takes one) gives the
+    eager result bit for bit on every replay, with eager work and synchronisations between
+    the replays."""
+    w = latents(N, K, 9700 + N + K)
+    x = make_acts(M, row_len(mode, K), 9710 + M + K)
+    gain, act = pro_args(mode, K, 9720 + K)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    xg, gg = up(x), None if gain is None else up(gain)
+    if mode is None:
+        xq, s = bl.bitlinear_quantize_act(xg)
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    ws = torch.empty((max(16, bl.bitlinear_forward_workspace_bytes(M, N, K)),), dtype=torch.uint8, device=DEV)
+
+    def run(stream=None):
+        if mode is None:
+            bl.bitlinear_forward(xq, s, packed, gamma, y=y, workspace=ws, stream=stream)
+        else:
+            bl.bitlinear_forward_f32(xg, packed, gamma, gg, EPS, act, y=y, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    eager = down(y).copy()
+    graph = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(graph, stream=st):
+            run(stream=st)
+    for i in range(3):
+        y.fill_(float("nan"))
+        ws.fill_(0xA5 + i)
+        other = torch.randn(64, 64, device=DEV) @ torch.randn(64, 64, device=DEV)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(down(y).view(np.int32), eager.view(np.int32)), "replay %d" % i
+        del other
