@@ -121,7 +121,7 @@ int bitlinear_quantize_act(const float* X, int64_t M, int64_t K, const float* ga
  *   acc       int32 [M][N] (written) or NULL
  * A packed field equal to 3 (never written by the packer) gives unspecified results.
  * Every token count gives the same bits: the kernel (vector dot products for a few
- * tokens, the int8 matrix cores for 2..16 tokens on the shapes where they are faster and
+ * tokens, the int8 matrix cores for 2..24 tokens on the shapes where they are faster and
  * for 16 tokens and more) only changes the order of exact integer additions.
  */
 int bitlinear_forward(const int8_t* Xq, const float* x_scale, int64_t M, int64_t K,

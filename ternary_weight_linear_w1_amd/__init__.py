@@ -253,7 +253,7 @@ def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=
                           residual=False, workspace=None, one_launch=False):
     """Fused quantize + product from fp32 activations [M][K] ([M][2K] when act == 2) -> fp32 y [M][N].
     residual=True adds the product to the given y. Where the product runs on the matrix cores
-    (from 16 tokens, and 3..15 tokens, or 2 for the largest matrices) the call goes through
+    (from 16 tokens; 3..15 tokens; 2 on the largest matrices) the call goes through
     bitlinear_forward_f32_ws (quantize into a workspace, then the matrix-core product); the
     workspace (uint8, at least bitlinear_forward_f32_workspace_bytes(M, N, K)) is allocated here
     when not given. one_launch=True calls the one-launch entry whatever M (same result)."""
