@@ -120,3 +120,25 @@ def test_100b_decode_m1_prequantized(i):
     accumulators: the launch shapes the pre-quantized dispatch picks for long rows."""
     name, N, K, mode = LAYER_100B[i]
     check_matrix(5, i + 16, N, K, mode, 1, fused=False)
+
+
+@pytest.mark.parametrize("M", [8, 32])
+@pytest.mark.parametrize("i", range(4))
+def test_100b_few_tokens(M, i):
+    """8 tokens (the few-token matrix-core kernel; down with its K split) and 32 tokens (the
+    tiled product; down with its K split), as bench.py times them; sampled outputs."""
+    name, N, K, mode = LAYER_100B[i]
+    check_matrix(5, i + 8 * M, N, K, mode, M, fused=False, sampled=True)
+
+
+LAYER_100B_TP8 = [("qkv", 1280, 8192, "plain"), ("o", 8192, 1024, "norm"), ("up", 3584, 8192, "plain"),
+                  ("down", 8192, 3584, "relu2norm")]
+
+
+@pytest.mark.parametrize("i", range(4))
+def test_100b_tp8_shard_m1(i):
+    """One GPU's share of the 100B slice under 8-way tensor parallelism at one token: the
+    fused call and the pre-quantized product, full outputs."""
+    name, N, K, mode = LAYER_100B_TP8[i]
+    check_matrix(6, i, N, K, mode, 1, fused=True)
+    check_matrix(6, i + 4, N, K, mode, 1, fused=False)
