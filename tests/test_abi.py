@@ -282,3 +282,21 @@ def test_attention_rejects_before_launch(L):
     assert call(vc=P(kc.value + 4096)) == ERR_ALIAS  # value cache inside the key cache
     assert call(ws=P(out.value)) == ERR_ALIAS
     assert call(pos=P(ws.value + 16)) == ERR_ALIAS   # device pos inside the workspace
+
+
+def test_peaks_library_exports_and_rejects():
+    """The benchmark's calibration kernels: both entries exported; invalid arguments are
+    rejected before any launch (no GPU needed)."""
+    if not os.path.exists(_build.PEAKS_LIB):
+        _build.build()
+    K = ctypes.CDLL(_build.PEAKS_LIB)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    K.bl_peak_stream_read.argtypes = [vp, i64, ci, ci, vp, vp]
+    K.bl_peak_mfma_i8.argtypes = [ci, ci, vp, vp]
+    a = P(1 << 24)
+    assert K.bl_peak_stream_read(None, 1024, 256, 4, a, None) == 1
+    assert K.bl_peak_stream_read(a, 1000, 256, 4, a, None) == 1           # not a multiple of 16
+    assert K.bl_peak_stream_read(P((1 << 24) + 8), 1024, 256, 4, a, None) == 1   # misaligned
+    assert K.bl_peak_stream_read(a, 1024, 256, 3, a, None) == 1           # unroll 2, 4 or 8
+    assert K.bl_peak_stream_read(a, 1024, 0, 4, a, None) == 1
+    assert K.bl_peak_mfma_i8(0, 256, a, None) == 1 and K.bl_peak_mfma_i8(10, 256, None, None) == 1
