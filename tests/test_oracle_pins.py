@@ -63,6 +63,22 @@ def test_gamma_floor_and_sign_pattern(ora):
     assert (q == signs.astype(np.int8)).all()
 
 
+def test_gamma_final_rounding_golden(ora, golden):
+    """gamma = fl32(S / n) with the binary64 quotient rounded once: two hand cases in which
+    rounding the sum (and n) to binary32 before dividing gives another binary32 value, one
+    with n = 3 and one with n = 2^24 + 1, where n itself is not a binary32 value. Catches
+    (float)S / (float)n and (float)S / n."""
+    cases = golden["gamma_final_rounding"]["cases"]
+    w = np.array(cases[0]["W"], np.float32)
+    assert ora.weight_scale(w) == F32(cases[0]["gamma"])
+    assert F32(cases[0]["gamma"]) != F32(cases[0]["gamma_if_sum_rounded_to_fp32_first"])
+    big = cases[1]
+    w = np.full(big["n"], F32(1.0) + F32(2.0 ** -23), np.float32)
+    assert ora.abs_sum(w) == 2.0 ** 24 + 3.0 + 2.0 ** -23
+    assert ora.weight_scale(w) == F32(big["gamma"])
+    assert F32(big["gamma"]) != F32(big["gamma_if_sum_and_n_rounded_to_fp32_first"])
+
+
 # ----------------------------------------------------------------------------- O2 codes
 
 def test_weight_ties_golden(ora, golden):
@@ -260,6 +276,18 @@ def test_forward_golden(ora, golden):
     assert r["y"][0, 0] == F32(32.0) * c and r["y"][0, 1] == F32(-191.0) * c
 
 
+def test_forward_rescale_order_golden(ora, golden):
+    """y = fl32(fl32(acc) * fl32(gamma / s)): a hand case (gamma = 1, s = 3, acc = 5) where
+    scaling by gamma and then dividing by s lands one unit lower. Catches the other
+    association and a product with an unrounded gamma / s."""
+    g = golden["rescale_order"]
+    acc, y = ora.forward(np.array(g["xq"], np.int8), np.array(g["s"], np.float32), np.array(g["codes"], np.int8),
+                         F32(g["gamma"]))
+    assert acc.tolist() == g["acc"]
+    assert y.tolist() == [[float(F32(v)) for v in row] for row in g["y"]]
+    assert y[0, 0] != F32(g["y0_if_scaled_by_gamma_then_divided_by_s"])
+
+
 def test_forward_acc_vs_integer_matmul(ora):
     """Accumulators against numpy's int64 matmul (a library primitive), non-square and
     ragged shapes so that a transposed operand cannot pass."""
@@ -428,8 +456,54 @@ def test_decode_layer_matches_dense_fp64_of_dequantized_operands(ora):
     assert np.array_equal(mid["o"][:, :32], mid["qkv"][:, 192:224])    # head 0 <- KV head 0's v
     d_o = dense(mid["o"], "o", gains["g_attn"], 0)
     assert close(mid["h1"], h.astype(np.float64) + d_o, np.abs(d_o).max())
+    d_u = dense(mid["h1"], "up", gains["g_post"], 0)      # the FFN reads h after attention
+    assert close(mid["u"], d_u, np.abs(d_u).max())
     d_d = dense(mid["u"], "down", gains["g_ffn"], 1)
     assert close(h2, mid["h1"].astype(np.float64) + d_d, np.abs(d_d).max())
+
+
+def test_decode_layer_cache_branch_at_position_one(ora):
+    """The real-context branch at position 1 with the QKV matrix's key rows zero: the new key
+    is exactly 0, as is the cached key of slot 0, so both scores are 0 and each softmax
+    weight is exactly 1/2. Query head h then outputs the mean of its group's cached value
+    (slot 0) and of the new value rounded to bf16; slot 1 of the key cache holds zeros and
+    slot 1 of the value cache the new value; h1 and the FFN read what the dense fp64 sublayers
+    give. Catches a dropped cache position, a wrong head-to-group map, the caches not updated
+    or updated at the wrong slot, and the FFN wired to the layer input."""
+    H, F, heads, kv, hd = 128, 192, 4, 2, 32
+    mats, gains, dims = _layer(ora, H, F, heads, kv, hd, False, 95)
+    w = datagen.gg_weights((heads + 2 * kv) * hd, H, 95)
+    w[heads * hd:(heads + kv) * hd] = 0.0                  # key rows
+    _, gamma, q = ora.pack_weights(w)
+    mats["qkv"] = (q, gamma)
+    M, cap = 2, 3
+    h = datagen.outlier_acts(M, H, 96)
+    kc = np.zeros((M, kv, cap, hd), np.uint16)
+    vc = ora.round_bf16(datagen.outlier_acts(M * kv * cap, hd, 97)).reshape(M, kv, cap, hd)
+    h2, mid = ora.decode_layer(h, mats, gains, dims, gated=False,
+                               cache=dict(k=kc, v=vc, pos=[1, 1], theta=10000.0))
+    assert not mid["qkv"][:, heads * hd:(heads + kv) * hd].any()
+    v_new = mid["qkv"][:, (heads + kv) * hd:].reshape(M, kv, hd)
+    v16 = ora.round_bf16(v_new)
+    expect = (ora.bf16_value(vc[:, :, 0]) + ora.bf16_value(v16)) / 2.0     # [M][kv][hd], exact in binary64
+    o = mid["o"].reshape(M, heads, hd)
+    for hh in range(heads):
+        assert (o[:, hh] == expect[:, hh // (heads // kv)].astype(np.float32)).all()
+    assert (mid["k"][:, :, 1] == 0).all() and (mid["v"][:, :, 1] == v16).all()
+    assert (mid["v"][:, :, 0] == vc[:, :, 0]).all() and (mid["v"][:, :, 2] == vc[:, :, 2]).all()
+
+    def dense(x, name, gain, act):
+        qq, gm = mats[name]
+        xq, s = ora.quantize_act_norm(x, gain, 1e-5, act)
+        return (xq.astype(np.float64) / s.astype(np.float64)[:, None]) @ (qq.astype(np.float64) * float(gm)).T
+
+    def close(a, b):
+        return (np.abs(a.astype(np.float64) - b) <= 1e-5 * np.abs(b - 0).max() + 1e-6 * np.abs(b)).all()
+
+    d_o = dense(mid["o"], "o", gains["g_attn"], 0)
+    assert close(mid["h1"] - h.astype(np.float64), d_o)
+    assert close(mid["u"], dense(mid["h1"], "up", gains["g_post"], 0))
+    assert close(h2 - mid["h1"].astype(np.float64), dense(mid["u"], "down", gains["g_ffn"], 1))
 
 
 # ----------------------------------------------------------------------------- 5 codes per byte
