@@ -1,24 +1,36 @@
 #!/usr/bin/env python3
 """Benchmark of the W1.58A8 BitLinear forward on one MI355X.
 
-Headline (`value`): HBM GB/s at M = 1 over one step = the four BitLinears of one
-BitNet-b1.58-2B-shaped layer at decode,
-    QKV 2560->3840 (plain absmax input), O 2560->2560 (subln RMSNorm input),
-    up 2560->6912 (plain), down 6912->2560 (ReLU^2 + subln RMSNorm input),
-each one launch of bitlinear_forward_f32 (input quantization fused), weights
-rotated over enough copies (>= 1 GiB) that every step streams them from HBM.
-Bytes per BitLinear = N*K/4 packed weights + 4 (gamma) + 4*M*K fp32 input
-[+ 4*K gain] + 4*M*N fp32 output.
+Headline (`value`): HBM GB/s at M = 1 over one step = one decode pass over a
+BitNet-100B-shaped slice of 4 layers, each layer's four BitLinears in order,
+    QKV 8192->10240 (plain absmax input), O 8192->8192 (subln RMSNorm input),
+    up 8192->28672 (plain), down 28672->8192 (ReLU^2 + subln RMSNorm input),
+each a call of the fused entry (input quantization, product and rescale), with its
+own latent weights per layer (620.8 MB packed per slice) and two copies of the whole
+slice rotated step by step (1.24 GB > 256 MB MALL + 32 MB L2), so every step streams its
+weights from HBM. Bytes per BitLinear = N*K/4 packed weights + 4 (gamma) + 4*M*K fp32
+input [+ 4*K gain] + 4*M*N fp32 output. Every graph is captured before the timed region;
+the timed region replays whole graphs and is timed with HIP events on the launch stream
+(bracketed by synchronizations), so `value` does not depend on the step count.
+
+Second headline (`prefill`): int8 TOPS at M = 2048 over one step = the four BitLinear
+products of a BitNet-2B-shaped layer (QKV 2560->3840, O 2560->2560, up 2560->6912,
+down 6912->2560) on pre-quantized activations, timed the same way; ops = 2*M*N*K.
 
 Also printed in the same JSON line:
-  roofline      the dominant kernel of the step (down projection) timed with HIP
-                events on the launch stream, vs 8 TB/s; `traffic` from committed
-                rocprofv3 FETCH_SIZE / WRITE_SIZE counters when they match the
+  roofline      the dominant kernel of the headline step (the down projection, the
+                longest launch) timed with HIP events around a graph of back-to-back
+                launches over >= 1 GiB of rotating weights, vs 8 TB/s; `traffic` from the
+                committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters when they match the
                 current kernel source, else null.
-  cpu_baseline  the CPU oracle on the same layer at M = 1 (single thread).
-  extra         per-matrix kernel rates for the 2B layer at M in {1,4,8}, the
-                100B-shaped slice at M in {1,64}, prefill at M in {512,2048}
-                (int8 TOPS), and the packing rate.
+  prefill       the M = 2048 figure with its own roofline (int8 matrix cores, 5 POPS).
+  cpu_baseline  the CPU oracle on the same bytes the GPU consumed (the first layer of the
+                slice, copied back from the device), one thread and then all threads of the
+                host share; its outputs are compared with the GPU's.
+  extra         per-matrix kernel rates: the slice's matrices, the 2B layer at M in {1,4,8},
+                the 100B matrices at M in {8, 32, 64}, prefill at M in {512, 2048}, five codes
+                per byte, decode attention, the 30-layer 2B decode stack, packing, and the
+                measured peaks of the calibration kernels.
 
 Other modes:
   --profile roofline   only the dominant kernel plus a copy kernel of known size
@@ -62,14 +74,15 @@ LAYER_100B = [("qkv", 10240, 8192, "plain"), ("o", 8192, 8192, "norm"), ("up", 2
 LAYER_100B_TP8 = [("qkv", 1280, 8192, "plain"), ("o", 8192, 1024, "norm"), ("up", 3584, 8192, "plain"),
                   ("down", 8192, 3584, "relu2norm")]
 
-DOMINANT = "down"
+SLICE_LAYERS = 4
+DOMINANT = "down"      # the longest launch of the headline step: 100B down projection, M = 1
 # What decides the measured GEMV's traffic: its kernel, the shared device helpers, and the
 # GEMV launch-shape section of the API file (from its "forward dispatch" banner to the MFMA
 # GEMM section), so edits elsewhere in the library do not invalidate the counter file.
 KERNEL_SRC = ["ternary_weight_linear_w1_amd/csrc/gemv.hpp", "ternary_weight_linear_w1_amd/csrc/device_common.hpp"]
 # the launch of one-token tiles (launch_k64 and the one-token dispatch) decides the measured kernel's grid
 DISPATCH_SRC = ("ternary_weight_linear_w1_amd/csrc/bitlinear_api.hip", "forward dispatch", "// Two tokens per tile")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_down_2B_M1_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_down_100B_M1_traffic.txt")
 
 
 def kernel_hash() -> str:
@@ -105,15 +118,15 @@ def log(*a):
 class Mat:
     """One BitLinear: packed weight copies, gamma, input, gain, output."""
 
-    def __init__(self, torch, bl, datagen, cfg, idx, name, N, K, mode, M, copies, dev):
+    def __init__(self, torch, bl, datagen, cfg, idx, name, N, K, mode, M, copies, dev, layer=0):
         self.name, self.N, self.K, self.mode, self.M = name, N, K, mode, M
-        w = datagen.gg_weights_torch(N, K, datagen.stream_id(cfg, 0, idx, 0), dev)
+        w = datagen.gg_weights_torch(N, K, datagen.stream_id(cfg, layer, idx, 0), dev)
         packed, gamma = bl.bitlinear_pack_weights(w)
         del w
         self.gamma = gamma
         self.copies = [packed] + [packed.clone() for _ in range(copies - 1)]
-        self.x = datagen.outlier_acts_torch(M, K, datagen.stream_id(cfg, 0, idx, 1), dev)
-        self.gain = datagen.gains_torch(K, datagen.stream_id(cfg, 0, idx, 2), dev) if "norm" in mode else None
+        self.x = datagen.outlier_acts_torch(M, K, datagen.stream_id(cfg, layer, idx, 1), dev)
+        self.gain = datagen.gains_torch(K, datagen.stream_id(cfg, layer, idx, 2), dev) if "norm" in mode else None
         self.relu2 = mode == "relu2norm"
         self.y = torch.empty((M, N), dtype=torch.float32, device=dev)
         self.xq = torch.empty((M, K), dtype=torch.int8, device=dev)
@@ -161,33 +174,93 @@ def time_kernel(torch, fn, copies, reps):
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(layer, seconds=10.0):
+def host_threads():
+    """Threads of this process's CPU share (at most 16, the share of one GPU on the box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(torch, mats, seconds=8.0):
+    """The CPU oracle, as it stands, on the bytes the GPU consumed: the packed weights, gamma,
+    inputs and gains of `mats` (one layer of the headline slice) are copied from the device,
+    unpacked by the oracle, and each BitLinear's quantization + int64 product + rescale is
+    run on the host, first on one thread, then with the output rows split over all threads
+    of this process's CPU share (the oracle is called once per row range; ctypes releases
+    the interpreter lock during the call). The oracle's outputs are compared with the
+    GPU's (bit for bit on the plain path, 1e-6 relative on the subln path)."""
+    import concurrent.futures
     import numpy as np
-    import datagen
     import oracle
-    mats = []
-    for idx, (name, N, K, mode) in enumerate(layer):
-        w = datagen.gg_weights(N, K, datagen.stream_id(2, 0, idx, 0))
-        _, gamma, q = oracle.pack_weights(w)
-        x = datagen.outlier_acts(1, K, datagen.stream_id(2, 0, idx, 1))
-        gain = datagen.gains(K, datagen.stream_id(2, 0, idx, 2)) if "norm" in mode else None
-        mats.append((q, gamma, x, gain, mode == "relu2norm", layer_bytes(N, K, 1, mode)))
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        for q, gamma, x, gain, relu2, _ in mats:
-            if gain is None and not relu2:
-                xq, s = oracle.quantize_act(x)
+    host = []
+    for m in mats:
+        packed = m.copies[0].cpu().numpy()
+        q, bad = oracle.unpack(packed, m.K)
+        assert bad == 0
+        x = m.x.cpu().numpy()
+        gain = None if m.gain is None else m.gain.cpu().numpy()
+        host.append((m, q, float(m.gamma.cpu().numpy()[0]), x, gain, m.y.cpu().numpy()))
+
+    def quant(x, gain, mode):
+        if mode == "plain":
+            return oracle.quantize_act(x)
+        return oracle.quantize_act_norm(x, gain, EPS, 1 if mode == "relu2norm" else 0)
+
+    # parity of the sample on the GPU's own bytes
+    match = {}
+    for m, q, gamma, x, gain, ygpu in host:
+        xq, s = quant(x, gain, m.mode)
+        _, y = oracle.forward(xq, s, q, gamma)
+        if m.mode == "plain":
+            match[m.name] = bool(np.array_equal(y, ygpu))
+        else:
+            match[m.name] = bool(np.all(np.abs(y.astype(np.float64) - ygpu) <= 1e-6 * np.abs(y.astype(np.float64))))
+    step_bytes = sum(m.bytes() for m, *_ in host)
+
+    def one_pass(pool=None, nthreads=1):
+        for m, q, gamma, x, gain, _ in host:
+            xq, s = quant(x, gain, m.mode)
+            if pool is None:
+                oracle.forward(xq, s, q, gamma)
             else:
-                xq, s = oracle.quantize_act_norm(x, gain, EPS, relu2)
-            oracle.forward(xq, s, q, gamma)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per_step = sum(m[5] for m in mats)
-    return {"value": round(per_step * steps / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d steps of the 2B layer's four BitLinears at M=1 (quantize + int32 product + rescale on "
-                      "unpacked codes, plain C, one thread), %.1f s" % (steps, el)}
+                bounds = np.linspace(0, m.N, nthreads + 1).astype(int)
+                list(pool.map(lambda r: oracle.forward(xq, s, q[bounds[r]:bounds[r + 1]], gamma), range(nthreads)))
+
+    def timed(pool, nthreads, budget):
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            one_pass(pool, nthreads)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return passes, el
+
+    p1, e1 = timed(None, 1, seconds)
+    T = host_threads()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=T) as pool:
+        pT, eT = timed(pool, T, seconds)
+    names = "/".join("%s %dx%d" % (m.name, m.N, m.K) for m, *_ in host)
+    return {"value": round(step_bytes * pT / eT / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": "%d passes over layer 0 of the 100B slice at M=1 (%s; %.1f MB per pass, the bytes the GPU "
+                      "consumed), quantize + int64 product + rescale on oracle-unpacked codes, output rows split over "
+                      "%d threads, %.1f s" % (pT, names, step_bytes / 1e6, T, eT),
+            "single_thread": {"value": round(step_bytes * p1 / e1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": "%d passes, %.1f s" % (p1, e1)},
+            "cpu_model": cpu_model(), "threads_available": host_threads(),
+            "oracle_build": "gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math (plain loops, no intrinsics)",
+            "matches_gpu": match}
 
 
 # ----------------------------------------------------------------------------- traffic
@@ -261,7 +334,10 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
 
     fe = per_kernel(fetch_csv, "FETCH_SIZE")
     wr = per_kernel(write_csv, "WRITE_SIZE")
-    gk = [k for k in fe if "gemv_k64_kernel" in k]
+    # the measured kernel: the library kernel launched most often (200 times in --profile
+    # roofline; the packing kernels of the setup run a few times)
+    lib_k = [k for k in fe if "bl::" in k]
+    gk = [max(lib_k, key=lambda k: len(fe[k]))] if lib_k else []
     ck = [k for k in fe if "copy" in k.lower()]
     if len(gk) != 1 or not ck:
         raise SystemExit("could not identify kernels: %s" % list(fe))
@@ -274,10 +350,11 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
     g_write_kib = sum(wr[gk[0]]) / len(wr[gk[0]])
     g_fetch = g_fetch_kib * 1024.0 * f_factor
     g_write = g_write_kib * 1024.0 * w_factor
-    N, K, mode = [(n, k, m) for (nm, n, k, m) in LAYER_2B if nm == DOMINANT][0]
+    N, K, mode = [(n, k, m) for (nm, n, k, m) in LAYER_100B if nm == DOMINANT][0]
     alg = layer_bytes(N, K, 1, mode)
     with open(out, "w") as f:
-        f.write("# HBM traffic of the down-projection GEMV (2B layer, 6912->2560, M=1, fused ReLU^2+subln input)\n")
+        f.write("# HBM traffic of the down-projection product (100B slice, %d->%d, M=1, fused ReLU^2+subln input)\n"
+                % (K, N))
         f.write("# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by\n")
         f.write("# the same counter read for a plain copy kernel of %d bytes read and written.\n" % copy_bytes)
         f.write("# commands:\n")
@@ -303,8 +380,8 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--profile", choices=["none", "roofline"], default="none")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary configurations")
     ap.add_argument("--attention-only", action="store_true",
@@ -318,7 +395,7 @@ def main():
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_CSV", "OUT"),
                     help="matrix-core busy fraction per GEMM launch from a rocprofv3 --pmc pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_CSV", "STATS_CSV", "OUT"))
     ap.add_argument("--trace-command", default="--steps 80 --warmup 8 --no-extra --no-cpu-baseline",
@@ -345,7 +422,7 @@ def main():
     import ternary_weight_linear_w1_amd as bl
     from ternary_weight_linear_w1_amd import _build
 
-    if not os.path.exists(_build.LIB):
+    if not _build.up_to_date():
         _build.build()
     bl.lib()
     if not torch.cuda.is_available():
@@ -366,15 +443,11 @@ def main():
         print(json.dumps(run_few(torch, bl, datagen, dev)))
         return 0
 
-    # ---- the 2B layer at M = 1
-    layer_copy_bytes = sum(N * K // 4 for _, N, K, _ in LAYER_2B)
-    G = 8
-    C = n_copies(layer_copy_bytes, G)
-    log("setup: 2B layer, %d rotating weight copies (%.2f GB)" % (C, C * layer_copy_bytes / 1e9))
-    mats = [Mat(torch, bl, datagen, 2, i, *spec, 1, C, dev) for i, spec in enumerate(LAYER_2B)]
-    dom = [m for m in mats if m.name == DOMINANT][0]
-
+    # ---- headline: the 100B-shaped slice at M = 1
     if args.profile == "roofline":
+        N, K, mode = [(n, k, md) for (nm, n, k, md) in LAYER_100B if nm == DOMINANT][0]
+        C = n_copies(N * K // 4)
+        dom = Mat(torch, bl, datagen, 5, 3, DOMINANT, N, K, mode, 1, C, dev)
         for i in range(200):
             dom.fused(bl, i % C)
         src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev)
@@ -385,99 +458,236 @@ def main():
         print(json.dumps({"profile": "roofline", "kernel_launches": 200, "copy_bytes": args.copy_bytes}))
         return 0
 
-    step_bytes = sum(m.bytes() for m in mats)
-
-    def step(c):
-        for m in mats:
-            m.fused(bl, c)
-
-    graphs = []
-    for gi in range(C // G):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for c in range(gi * G, gi * G + G):
-                step(c)
-        graphs.append(g)
-    singles = {}
-
-    def run_steps(start, count):
-        s = start
-        end = start + count
-        while s < end:
-            c = s % C
-            if c % G == 0 and end - s >= G:
-                graphs[c // G].replay()
-                s += G
-            else:
-                if c not in singles:
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g):
-                        step(c)
-                    singles[c] = g
-                singles[c].replay()
-                s += 1
-        return s
-
-    log("warmup %d steps" % args.warmup)
-    pos = run_steps(0, args.warmup)
-    torch.cuda.synchronize()
-    log("timing %d steps" % args.steps)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    run_steps(pos, args.steps)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_s = ev0.elapsed_time(ev1) * 1e-3
-    ms_per_step = wall / args.steps * 1e3
-    value = step_bytes * args.steps / wall / 1e9
-
-    # ---- roofline of the dominant kernel (down projection), events on the launch stream
-    avg_s = time_kernel(torch, lambda c: dom.fused(bl, c), C, 400)
-    dom_bytes = dom.bytes()
-    achieved = dom_bytes / avg_s / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
-                "kernel": "bitlinear_forward_f32 down 6912->2560 (ReLU^2+subln input), M=1",
-                "algorithmic_bytes": dom_bytes, "avg_us": round(avg_s * 1e6, 3),
-                "timing": "HIP events around a graph of 400 back-to-back launches on the launch stream"}
-    log("value %.1f GB/s, %.4f ms/step; dominant kernel %.2f us = %.1f GB/s" %
-        (value, ms_per_step, avg_s * 1e6, achieved))
-
-    extra = {"step_bytes": step_bytes, "step_gpu_ms": round(gpu_s / args.steps * 1e3, 5),
-             "weight_copies": C}
-    # per-matrix kernel rates at M = 1 (fused)
-    extra["2B_M1_fused"] = {}
-    for m in mats:
-        a = time_kernel(torch, lambda c, m=m: m.fused(bl, c), C, 200)
-        extra["2B_M1_fused"][m.name] = {"us": round(a * 1e6, 3), "GB/s": round(m.bytes() / a / 1e9, 1)}
-    del graphs, singles
-
-    if not args.no_extra:
-        extra.update(run_extra(torch, bl, datagen, dev, mats))
+    head = run_headline(torch, bl, datagen, dev, args.steps, args.warmup)
+    slice_mats = head.pop("_mats")
+    roofline = head.pop("_roofline")
+    extra = head.pop("_extra")
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(LAYER_2B, args.cpu_seconds)
+        log("cpu baseline (oracle) on layer 0 of the slice ...")
+        cpu = cpu_baseline(torch, slice_mats[0], args.cpu_seconds)
+        log("cpu baseline: %s" % cpu)
+    del slice_mats
+    torch.cuda.empty_cache()
+
+    prefill = run_prefill_headline(torch, bl, datagen, dev, 2048, args.steps, args.warmup)
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        extra.update(run_extra(torch, bl, datagen, dev))
 
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": head["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-        "config": {"workload": "BitNet-b1.58-2B-shaped layer BitLinears at decode, M=1: QKV 2560->3840, "
-                               "O 2560->2560 (subln input), up 2560->6912, down 6912->2560 (ReLU^2+subln input); "
-                               "fused input quantization; GG(0.846) latents (42/29/29 ternary split); "
-                               "%d rotating weight copies so weights stream from HBM" % C,
-                   "M": 1, "entry": "bitlinear_forward_f32", "graph": "HIP graph of 8 steps"},
+        "config": head["config"],
         "roofline": roofline,
+        "prefill": prefill,
         "cpu_baseline": cpu,
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def graph_of(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def timed_replays(torch, graphs_in_order):
+    """Replays the given graphs back to back between synchronizations; returns (GPU seconds
+    from HIP events on the launch stream, host wall seconds)."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for g in graphs_in_order:
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) * 1e-3, wall
+
+
+def rotation_plan(graphs_pair, graphs_single, start, count):
+    """Graph sequence for `count` steps starting at weight copy `start` (0 or 1): pairs of
+    steps (copy c then the other one), then one single step if count is odd."""
+    seq, c = [], start
+    for _ in range(count // 2):
+        seq.append(graphs_pair[c])
+    if count % 2:
+        seq.append(graphs_single[c])
+    return seq
+
+
+def run_headline(torch, bl, datagen, dev, steps, warmup):
+    """The 100B-shaped slice (4 layers x QKV, O, up, down), M = 1, fused entry per BitLinear,
+    two copies of the whole slice (1.24 GB) alternating step by step."""
+    log("setup: 100B slice, %d layers, 2 copies of the packed weights" % SLICE_LAYERS)
+    mats = [[Mat(torch, bl, datagen, 5, i, name, N, K, mode, 1, 2, dev, layer=li)
+             for i, (name, N, K, mode) in enumerate(LAYER_100B)] for li in range(SLICE_LAYERS)]
+    flat = [m for row in mats for m in row]
+    step_bytes = sum(m.bytes() for m in flat)
+    packed_bytes = sum(m.N * m.K // 4 for m in flat)
+
+    def step(c):
+        for m in flat:
+            m.fused(bl, c)
+
+    for c in (0, 1):          # eager pass: every kernel loaded before capture
+        step(c)
+    torch.cuda.synchronize()
+    pair = [graph_of(torch, lambda: (step(0), step(1))), graph_of(torch, lambda: (step(1), step(0)))]
+    single = [graph_of(torch, lambda: step(0)), graph_of(torch, lambda: step(1))]
+    log("warmup %d steps" % warmup)
+    timed_replays(torch, rotation_plan(pair, single, 0, warmup))
+    log("timing %d steps" % steps)
+    gpu_s, wall = timed_replays(torch, rotation_plan(pair, single, warmup % 2, steps))
+    value = step_bytes * steps / gpu_s / 1e9
+    ms_per_step = gpu_s / steps * 1e3
+    log("value %.1f GB/s (%.4f ms/step by events; %.4f ms/step by host wall clock)" %
+        (value, ms_per_step, wall / steps * 1e3))
+    del pair, single
+
+    # per-matrix launches of the step (fused entry), each over >= 1 GiB of rotating weights:
+    # the slice's 8 instances of the matrix (4 layers x 2 copies) plus clones
+    per = {}
+    dom_avg = None
+    for i, (name, N, K, mode) in enumerate(LAYER_100B):
+        inst = [(row[i], c) for row in mats for c in (0, 1)]
+        extra_c = max(0, n_copies(N * K // 4) - len(inst))
+        clones = [mats[0][i].copies[0].clone() for _ in range(extra_c)]
+        m0 = mats[0][i]
+        rot = [lambda m=m, c=c: m.fused(bl, c) for m, c in inst] + \
+              [lambda w=w: bl.bitlinear_forward_f32(m0.x, w, m0.gamma, m0.gain, EPS, m0.relu2, y=m0.y) for w in clones]
+        a = time_kernel(torch, lambda j: rot[j](), len(rot), 200)
+        b = m0.bytes()
+        per[name] = {"us": round(a * 1e6, 3), "GB/s": round(b / a / 1e9, 1), "frac_hbm": round(b / a / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": b, "rotating_copies": len(rot)}
+        if name == DOMINANT:
+            dom_avg, dom_bytes = a, b
+        del clones, rot
+        torch.cuda.empty_cache()
+    log("slice per-matrix (fused, M=1): %s" % per)
+    achieved = dom_bytes / dom_avg / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
+                "kernel": "bitlinear_forward_f32 down 28672->8192 (ReLU^2+subln input), M=1",
+                "algorithmic_bytes": dom_bytes, "avg_us": round(dom_avg * 1e6, 3),
+                "timing": "HIP events around a graph of 200 back-to-back launches on the launch stream, "
+                          "weights rotating over >= 1 GiB"}
+    step_us = sum(v["us"] for v in per.values()) * SLICE_LAYERS
+    config = {"workload": "BitNet-b1.58-100B-shaped layer slice at decode, M=1: %d layers x [QKV 8192->10240 "
+                          "(plain absmax input), O 8192->8192 (subln input), up 8192->28672 (plain), down "
+                          "28672->8192 (ReLU^2+subln input)], one fused BitLinear call each (quantize + "
+                          "W1.58A8 product + rescale), GG(0.846) latents per layer (42/29/29 ternary split), "
+                          "2 copies of the slice alternating (%.2f GB) so weights stream from HBM"
+                          % (SLICE_LAYERS, 2 * packed_bytes / 1e9),
+              "M": 1, "entry": "bitlinear_forward_f32", "step_bytes": step_bytes, "packed_bytes": packed_bytes,
+              "graph": "one HIP graph per two steps (both copies), captured before timing",
+              "timing": "HIP events around the replays of the timed steps; %.4f ms/step by host wall clock"
+                        % (wall / steps * 1e3)}
+    extra = {"100B_slice_M1_per_matrix_fused": per,
+             "100B_slice_sum_of_launches_us": round(step_us, 2),
+             "100B_slice_step_us": round(ms_per_step * 1e3, 2)}
+    return {"value": round(value, 2), "ms_per_step": round(ms_per_step, 5), "config": config, "_mats": mats,
+            "_roofline": roofline, "_extra": extra}
+
+
+def run_prefill_headline(torch, bl, datagen, dev, M, steps, warmup):
+    """int8 TOPS at M tokens over one step = the four products of the 2B-shaped layer on
+    pre-quantized activations (the int8 matrix-core GEMM), two weight copies alternating,
+    graphs captured before timing, HIP events around the timed replays."""
+    log("setup: prefill M=%d on the 2B layer shapes" % M)
+    mats = []
+    for i, (name, N, K, mode) in enumerate(LAYER_2B):
+        m = Mat(torch, bl, datagen, 4, i + 4, name, N, K, mode, M, 2, dev)
+        m.x = datagen.heavy_channel_acts_torch(M, K, datagen.stream_id(4, 1, i, 1), dev)
+        m.prequant(bl)
+        mats.append(m)
+    ops = sum(2.0 * M * m.N * m.K for m in mats)
+
+    def step(c):
+        for m in mats:
+            m.forward(bl, c)
+
+    for c in (0, 1):
+        step(c)
+    torch.cuda.synchronize()
+    pair = [graph_of(torch, lambda: (step(0), step(1))), graph_of(torch, lambda: (step(1), step(0)))]
+    single = [graph_of(torch, lambda: step(0)), graph_of(torch, lambda: step(1))]
+    timed_replays(torch, rotation_plan(pair, single, 0, warmup))
+    gpu_s, wall = timed_replays(torch, rotation_plan(pair, single, warmup % 2, steps))
+    tops = ops * steps / gpu_s / 1e12
+    del pair, single
+    per = {}
+    for m in mats:
+        a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), 2, 20)
+        o = 2.0 * M * m.N * m.K
+        per[m.name] = {"us": round(a * 1e6, 2), "TOPS": round(o / a / 1e12, 1),
+                       "frac_int8_peak": round(o / a / 1e12 / INT8_PEAK_TOPS, 4)}
+    dom = max(per, key=lambda k: per[k]["us"])
+    dm = [m for m in mats if m.name == dom][0]
+    a = per[dom]["us"] * 1e-6
+    achieved = 2.0 * M * dm.N * dm.K / a / 1e12
+    out = {"metric": "int8 TOPS @M=2048 (W1.58A8 prefill product)", "value": round(tops, 1), "unit": "TOPS",
+           "ms_per_step": round(gpu_s / steps * 1e3, 5), "steps": steps, "warmup": warmup,
+           "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+           "config": {"workload": "BitNet-b1.58-2B-shaped layer products at prefill, M=%d: QKV 2560->3840, "
+                                  "O 2560->2560, up 2560->6912, down 6912->2560 on pre-quantized int8 activations "
+                                  "(N(0,1) with 1%% Student-t(3) channels), GG(0.846) latents" % M,
+                      "M": M, "entry": "bitlinear_forward", "ops_per_step": ops,
+                      "timing": "HIP events around graph replays captured before timing; %.4f ms/step by host "
+                                "wall clock" % (wall / steps * 1e3)},
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                        "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                        "kernel": "bitlinear_forward %s %d->%d, M=%d (int8 matrix-core GEMM)" % (dom, dm.K, dm.N, M),
+                        "avg_us": per[dom]["us"],
+                        "timing": "HIP events around a graph of 20 back-to-back launches (two weight copies)"},
+           "per_matrix": per}
+    log("prefill M=%d: %.1f TOPS (%.4f ms/step); per matrix %s" % (M, tops, gpu_s / steps * 1e3, per))
+    del mats
+    return out
+
+
+def run_2b_layer(torch, bl, datagen, dev, steps=400):
+    """One BitNet-2B-shaped layer's four BitLinears at M = 1 (fused entry each), weights
+    rotating over >= 1 GiB of copies, graphs of 8 steps captured before timing; and each
+    matrix's launch alone (graph of back-to-back launches)."""
+    layer_copy_bytes = sum(N * K // 4 for _, N, K, _ in LAYER_2B)
+    G = 8
+    C = n_copies(layer_copy_bytes, G)
+    mats = [Mat(torch, bl, datagen, 2, i, *spec, 1, C, dev) for i, spec in enumerate(LAYER_2B)]
+    step_bytes = sum(m.bytes() for m in mats)
+
+    def steps_of(c0):
+        for c in range(c0, c0 + G):
+            for m in mats:
+                m.fused(bl, c)
+
+    steps_of(0)
+    torch.cuda.synchronize()
+    graphs = [graph_of(torch, lambda gi=gi: steps_of(gi * G)) for gi in range(C // G)]
+    timed_replays(torch, graphs)
+    reps = max(1, steps // (G * len(graphs)))
+    gpu_s, _ = timed_replays(torch, graphs * reps)
+    n = G * len(graphs) * reps
+    out = {"us_per_step": round(gpu_s / n * 1e6, 3), "GB/s": round(step_bytes * n / gpu_s / 1e9, 1),
+           "step_bytes": step_bytes, "steps": n, "weight_copies": C}
+    del graphs
+    per = {}
+    for m in mats:
+        a = time_kernel(torch, lambda c, m=m: m.fused(bl, c), C, 200)
+        per[m.name] = {"us": round(a * 1e6, 3), "GB/s": round(m.bytes() / a / 1e9, 1)}
+    out["per_matrix_fused"] = per
+    log("extra 2B layer M=1: %s" % out)
+    del mats
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_cfg1(torch, bl, datagen, dev):
@@ -508,7 +718,7 @@ def run_peaks(torch, dev):
     M = 2048 (dense int8 weights: 4x the bytes of the packed ternary ones)."""
     import ctypes
     from ternary_weight_linear_w1_amd import _build
-    if not os.path.exists(_build.PEAKS_LIB):
+    if not _build.up_to_date():
         _build.build()
     P = ctypes.CDLL(_build.PEAKS_LIB)
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -629,8 +839,9 @@ def run_few(torch, bl, datagen, dev):
     return res
 
 
-def run_extra(torch, bl, datagen, dev, mats2b):
+def run_extra(torch, bl, datagen, dev):
     res = {}
+    res["2B_layer_M1_step"] = run_2b_layer(torch, bl, datagen, dev)
     res["cfg1_single_M1"] = run_cfg1(torch, bl, datagen, dev)
     res["measured_peaks"] = run_peaks(torch, dev)
     torch.cuda.empty_cache()

@@ -226,7 +226,7 @@ int bitlinear_forward_ws(const int8_t* Xq, const float* x_scale, int64_t M, int6
  *
  * bitlinear_forward5 is bitlinear_forward on W_packed5: the same exact int32 sums and
  * the same rescale, y[t][n] = fl32(fl32(acc[t][n]) * fl32(gamma / s_t)). K must be a
- * multiple of 16 and at most 131072 (a token's codes are staged in LDS), N at most
+ * multiple of 16 and at most 131072 (a token's codes are staged in LDS), N below
  * 2^27; Xq and W_packed5 16-byte aligned. A byte above
  * 242 (never written by the packer) gives unspecified results.
  */

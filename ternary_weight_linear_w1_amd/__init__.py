@@ -118,6 +118,18 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream):
+    """A tensor allocated here for the call's outputs or scratch. The caching allocator
+    ties a block to the stream that was current at allocation; when the work goes to
+    another stream, the block is marked as used there too, so that it is not handed out
+    again before that stream's kernels are done with it."""
+    import torch
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+    return t
+
+
 def _need(t, dtype, name, ndim=None, shape=None):
     """Device, dtype, contiguity and (when given) rank and exact shape of a tensor argument:
     the library trusts the sizes it is given, so a short buffer must not get through."""
@@ -146,14 +158,14 @@ def bitlinear_pack_weights(W, packed=None, gamma=None, workspace=None, stream=No
     _need(W, torch.float32, "W", 2)
     N, K = W.shape
     if packed is None:
-        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+        packed = _empty((N, K // 4), torch.uint8, W.device, stream)
     _need(packed, torch.uint8, "packed", shape=(N, K // 4))
     if gamma is None:
-        gamma = torch.empty((1,), dtype=torch.float32, device=W.device)
+        gamma = _empty((1,), torch.float32, W.device, stream)
     _need(gamma, torch.float32, "gamma", shape=(1,))
     nbytes = bitlinear_pack_workspace_bytes(N, K)
     if workspace is None:
-        workspace = torch.empty((max(nbytes, 8),), dtype=torch.uint8, device=W.device)
+        workspace = _empty((max(nbytes, 8),), torch.uint8, W.device, stream)
     _check(lib().bitlinear_pack_weights(_ptr(W), N, K, _ptr(packed), _ptr(gamma), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(stream)),
            "bitlinear_pack_weights")
@@ -181,10 +193,10 @@ def bitlinear_quantize_act(X, gain=None, eps: float = 1e-5, act=0, xq=None, scal
     if gain is not None:
         _need(gain, torch.float32, "gain", shape=(K,))
     if xq is None:
-        xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+        xq = _empty((M, K), torch.int8, X.device, stream)
     _need(xq, torch.int8, "xq", shape=(M, K))
     if scale is None:
-        scale = torch.empty((M,), dtype=torch.float32, device=X.device)
+        scale = _empty((M,), torch.float32, X.device, stream)
     _need(scale, torch.float32, "scale", shape=(M,))
     _check(lib().bitlinear_quantize_act(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(xq),
                                         _ptr(scale), _stream(stream)), "bitlinear_quantize_act")
@@ -218,17 +230,17 @@ def bitlinear_forward(Xq, x_scale, W_packed, gamma, y=None, acc=None, stream=Non
         _need(y, torch.float32, "y", shape=(M, N))
     else:
         if y is None:
-            y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+            y = _empty((M, N), torch.float32, Xq.device, stream)
         _need(y, torch.float32, "y", shape=(M, N))
         if acc is True:
-            acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+            acc = _empty((M, N), torch.int32, Xq.device, stream)
         if isinstance(acc, torch.Tensor):
             _need(acc, torch.int32, "acc", shape=(M, N))
     accp = _ptr(acc if isinstance(acc, torch.Tensor) else None)
     need = bitlinear_forward_workspace_bytes(M, N, K)
     if split and (need > 0 or workspace is not None):
         if workspace is None:
-            workspace = torch.empty((need,), dtype=torch.uint8, device=Xq.device)
+            workspace = _empty((need,), torch.uint8, Xq.device, stream)
         _need(workspace, torch.uint8, "workspace", 1)
         if workspace.numel() < need:
             raise ValueError("workspace must hold %d bytes" % need)
@@ -274,13 +286,13 @@ def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=
         fn, name = lib().bitlinear_forward_f32_residual, "bitlinear_forward_f32_residual"
     else:
         if y is None:
-            y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+            y = _empty((M, N), torch.float32, X.device, stream)
         _need(y, torch.float32, "y", shape=(M, N))
         fn, name = lib().bitlinear_forward_f32, "bitlinear_forward_f32"
     need = bitlinear_forward_f32_workspace_bytes(M, N, K)
     if not one_launch and (need > 0 or workspace is not None):
         if workspace is None:
-            workspace = torch.empty((need,), dtype=torch.uint8, device=X.device)
+            workspace = _empty((need,), torch.uint8, X.device, stream)
         _need(workspace, torch.uint8, "workspace", 1)
         if workspace.numel() < need:
             raise ValueError("workspace must hold %d bytes" % need)
@@ -305,7 +317,7 @@ def bitlinear_repack5(W_packed, out=None, stream=None):
     N, K = W_packed.shape[0], W_packed.shape[1] * 4
     rb = bitlinear_packed5_row_bytes(K)
     if out is None:
-        out = torch.empty((N, rb), dtype=torch.uint8, device=W_packed.device)
+        out = _empty((N, rb), torch.uint8, W_packed.device, stream)
     _need(out, torch.uint8, "out", shape=(N, rb))
     _check(lib().bitlinear_repack5(_ptr(W_packed), N, K, _ptr(out), _stream(stream)), "bitlinear_repack5")
     return out
@@ -323,10 +335,10 @@ def bitlinear_forward5(Xq, x_scale, W_packed5, gamma, y=None, acc=None, stream=N
     _need(x_scale, torch.float32, "x_scale", shape=(M,))
     _need(gamma, torch.float32, "gamma", shape=(1,))
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+        y = _empty((M, N), torch.float32, Xq.device, stream)
     _need(y, torch.float32, "y", shape=(M, N))
     if acc is True:
-        acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+        acc = _empty((M, N), torch.int32, Xq.device, stream)
     if isinstance(acc, torch.Tensor):
         _need(acc, torch.int32, "acc", shape=(M, N))
     _check(lib().bitlinear_forward5(_ptr(Xq), _ptr(x_scale), M, K, _ptr(W_packed5), _ptr(gamma), N, _ptr(y),
@@ -359,11 +371,11 @@ def bitlinear_attention_decode(qkv, k_cache, v_cache, pos, heads: int, kv_heads:
     _need(v_cache, torch.bfloat16, "v_cache", shape=(M, kv_heads, capacity, d))
     _need(pos, torch.int32, "pos", shape=(M,))
     if out is None:
-        out = torch.empty((M, heads * d), dtype=torch.float32, device=qkv.device)
+        out = _empty((M, heads * d), torch.float32, qkv.device, stream)
     _need(out, torch.float32, "out", shape=(M, heads * d))
     need = bitlinear_attention_workspace_bytes(M, heads, capacity)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=qkv.device)
+        workspace = _empty((max(need, 1),), torch.uint8, qkv.device, stream)
     _need(workspace, torch.uint8, "workspace", 1)
     _check(lib().bitlinear_attention_decode(_ptr(qkv), _ptr(k_cache), _ptr(v_cache), _ptr(pos), M, int(heads),
                                             int(kv_heads), d, capacity, float(theta), _ptr(out), _ptr(workspace),

@@ -13,6 +13,7 @@ DEPS = SOURCES + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(
     os.path.join(os.path.dirname(HERE), "include", "bitlinear.h")]
 PEAKS_LIB = os.path.join(HERE, "libbitlinear_peaks.so")
 PEAKS_SOURCES = [os.path.join(CSRC, "peaks.hip")]
+PEAKS_DEPS = PEAKS_SOURCES
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -49,11 +50,16 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def up_to_date() -> bool:
-    if not os.path.exists(LIB):
+def _newer_than(out, deps) -> bool:
+    if not os.path.exists(out):
         return False
-    t = os.path.getmtime(LIB)
-    return all(os.path.getmtime(p) <= t for p in DEPS)
+    t = os.path.getmtime(out)
+    return all(os.path.getmtime(p) <= t for p in deps)
+
+
+def up_to_date() -> bool:
+    """Both libraries exist and are newer than every source they are built from."""
+    return _newer_than(LIB, DEPS) and _newer_than(PEAKS_LIB, PEAKS_DEPS)
 
 
 if __name__ == "__main__":

@@ -365,7 +365,7 @@ int64_t mfma_phase_windows(int64_t M, int64_t K, int64_t rg_per_block)
 
 bool mfma_small_shape(int64_t M, int64_t N, int64_t K, int64_t cus)
 {
-    if (M < 2 || M > kMfmaMaxTokens || (K % 64) != 0 || N > (int64_t(1) << 27))
+    if (M < 2 || M > kMfmaMaxTokens || (K % 64) != 0 || N >= (int64_t(1) << 27))
         return false;
     const int64_t nk = N * K;
     if ((M == 2 && nk < (int64_t(128) << 20)) || (M >= 16 && nk >= (int64_t(64) << 20)))
@@ -401,8 +401,9 @@ template <bool FUSED>
 void dispatch_forward(const bl::FwdArgs& a, bool chunk_ok, hipStream_t stream)
 {
     // 32-bit buffer offsets: a token tile of outputs (4 rows of N floats) must stay
-    // below 2 GiB.
-    chunk_ok = chunk_ok && a.N <= (int64_t(1) << 27);
+    // below 2 GiB, and at or below the out-of-range offset that masked lanes use
+    // (4 * 4 * (2^27 - 1) bytes == kOob), so that their stores are dropped.
+    chunk_ok = chunk_ok && a.N < (int64_t(1) << 27);
     if (chunk_ok) {
         if (a.M == 1 && dispatch_mt1<FUSED>(a, stream))
             return;
@@ -833,8 +834,10 @@ int bitlinear_forward5(const int8_t* Xq, const float* x_scale, int64_t M, int64_
         return st;
     if ((st = check_nk(N, K)) != BITLINEAR_OK)
         return st;
-    // a staged row of codes must fit in LDS (and the widest tile covers 2048 chunks)
-    if ((K % 16) != 0 || K > 131072 || M > kMaxElems / N || N > (int64_t(1) << 27))
+    // a staged row of codes must fit in LDS (and the widest tile covers 2048 chunks); a
+    // 4-token tile of outputs must stay within the 32-bit buffer range, masked lanes
+    // storing at kOob past its end
+    if ((K % 16) != 0 || K > 131072 || M > kMaxElems / N || N >= (int64_t(1) << 27))
         return BITLINEAR_ERR_SHAPE;
     if (!aligned(Xq, 16) || !aligned(x_scale, 4) || !aligned(W_packed5, 16) || !aligned(gamma, 4) ||
         !aligned(Y, 4) || (acc && !aligned(acc, 4)))

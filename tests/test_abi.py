@@ -238,6 +238,11 @@ def test_five_per_byte_calls_reject_before_launch(L):
     assert f(*args(Xq=P(a + 4))) == ERR_ALIGN
     assert f(*args(W=P(3 * a + 4))) == ERR_ALIGN
     assert f(*args(Y=P(3 * a))) == ERR_ALIAS
+    # a 4-token tile of outputs (4 N floats) must end at or before the offset that masked
+    # lanes store to (2^31 - 16), so N = 2^27 is out of range and 2^27 - 1 passes the size
+    # checks (and then fails the overlap check of these fake buffers, still before a launch)
+    assert f(*args(N=1 << 27)) == ERR_SHAPE
+    assert f(*args(N=(1 << 27) - 1)) == ERR_ALIAS
 
 
 def test_attention_workspace_bytes(L):

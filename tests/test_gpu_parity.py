@@ -507,3 +507,31 @@ def test_products_graph_replay(M, N, K, mode):
         torch.cuda.synchronize()
         assert np.array_equal(down(y).view(np.int32), eager.view(np.int32)), "replay %d" % i
         del other
+
+
+def test_binding_scratch_survives_a_side_stream():
+    """Scratch the binding allocates for a call on a side stream (here the workspace of the
+    fused call at 32 tokens: codes and scales) must not be handed out again before that
+    stream is done with it. The side stream is held back by a bounded spin kernel, the
+    buffer is dropped when the call returns, and the current stream at once allocates the
+    same number of bytes and fills them; the product must still equal the one computed on
+    the current stream."""
+    M, N, K = 32, 1024, 2560
+    w = latents(N, K, 4242)
+    x = make_acts(M, K, 4243)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    X = up(x)
+    ref = bl.bitlinear_forward_f32(X, packed, gamma)
+    torch.cuda.synchronize()
+    need = bl.bitlinear_forward_f32_workspace_bytes(M, N, K)
+    assert need > 0
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)
+    bl.bitlinear_forward_f32(X, packed, gamma, y=y, stream=side)
+    junk = torch.empty((need,), dtype=torch.uint8, device=DEV)
+    junk.fill_(0x7F)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
