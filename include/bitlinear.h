@@ -182,6 +182,28 @@ int bitlinear_forward_f32_ws(const float* X, int64_t M, int64_t K, const float* 
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The fused call with a caller workspace, for callers that cannot allocate memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments (except the workspace) and result as bitlinear_forward_f32_ws, with
+ * the workspace taken from a fixed scratch array that the library holds in each device's
+ * memory from the time it is loaded until the process ends. It calls no allocating
+ * routine. Limit: the sizes may need at most BITLINEAR_NOALLOC_SCRATCH_BYTES of workspace
+ * (bitlinear_forward_f32_workspace_bytes(M, N, K) <= 32 MiB: the M x K codes, the M scales
+ * and any K-split partials; for example 2048 tokens with K = 8192 fit); larger sizes return
+ * BITLINEAR_ERR_WORKSPACE before anything is enqueued. Sizes that need no workspace (one
+ * token, and the sizes the one-launch product takes) do not touch the scratch. The first
+ * call on each device looks up that device's copy of the array (hipGetSymbolAddress; make
+ * that call outside graph capture); a failed lookup returns
+ * BITLINEAR_ERR_HIP. Every call on one device shares that device's array, which keeps the
+ * last call's contents: calls that may overlap on one device (several streams or host
+ * threads) race on it and must be ordered by the caller.
+ */
+#define BITLINEAR_NOALLOC_SCRATCH_BYTES (32u << 20)
+int bitlinear_forward_f32_noalloc(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
+                                  const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int residual,
+                                  hipStream_t stream);
+
+/*
  * The product with a caller workspace (the same operation and result as bitlinear_forward,
  * or bitlinear_forward_residual when residual != 0; "BitNet b1.58 深度解析" s.2.3).
  *

@@ -18,7 +18,8 @@ from ._build import LIB as _LIB_PATH
 __all__ = [
     "BitLinearError", "lib", "status_string", "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
     "bitlinear_quantize_act", "bitlinear_forward", "bitlinear_forward_f32", "bitlinear_forward_f32_workspace_bytes",
-    "bitlinear_forward_workspace_bytes", "bitlinear_attention_workspace_bytes",
+    "bitlinear_forward_workspace_bytes", "bitlinear_forward_f32_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "bitlinear_attention_workspace_bytes",
     "bitlinear_attention_decode", "EXPORTED",
 ]
 
@@ -33,6 +34,7 @@ EXPORTED = (
     "bitlinear_forward_f32_residual",
     "bitlinear_forward_f32_workspace_bytes",
     "bitlinear_forward_f32_ws",
+    "bitlinear_forward_f32_noalloc",
     "bitlinear_forward_workspace_bytes",
     "bitlinear_forward_ws",
     "bitlinear_packed5_row_bytes",
@@ -79,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward_f32_workspace_bytes.restype = ctypes.c_size_t
         L.bitlinear_forward_f32_ws.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, i64, vp, ci, vp, ctypes.c_size_t, vp]
         L.bitlinear_forward_f32_ws.restype = ci
+        L.bitlinear_forward_f32_noalloc.argtypes = [vp, i64, i64, vp, f32, ci, vp, vp, i64, vp, ci, vp]
+        L.bitlinear_forward_f32_noalloc.restype = ci
         L.bitlinear_forward_workspace_bytes.argtypes = [i64, i64, i64]
         L.bitlinear_forward_workspace_bytes.restype = ctypes.c_size_t
         L.bitlinear_forward_ws.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, ci, vp, ctypes.c_size_t, vp]
@@ -302,6 +306,33 @@ def bitlinear_forward_f32(X, W_packed, gamma, gain=None, eps: float = 1e-5, act=
         return y
     _check(fn(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(W_packed), _ptr(gamma), N, _ptr(y), _stream(stream)),
            name)
+    return y
+
+
+# Fixed scratch of bitlinear_forward_f32_noalloc (BITLINEAR_NOALLOC_SCRATCH_BYTES in the header).
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def bitlinear_forward_f32_noalloc(X, W_packed, gamma, y, gain=None, eps: float = 1e-5, act=0, stream=None,
+                                  residual=False):
+    """The fused call without any allocation, here or in the library: the library's fixed
+    per-device scratch serves as the workspace (sizes needing more than
+    NOALLOC_SCRATCH_BYTES are rejected). y must be given. Calls that may overlap on one
+    device share that scratch and must be ordered by the caller."""
+    import torch
+    _need(X, torch.float32, "X", 2)
+    _need(W_packed, torch.uint8, "W_packed", 2)
+    _need(gamma, torch.float32, "gamma", shape=(1,))
+    act, M, K = _act_mode(act, X)
+    if gain is not None:
+        _need(gain, torch.float32, "gain", shape=(K,))
+    N = W_packed.shape[0]
+    if W_packed.shape[1] * 4 != K:
+        raise ValueError("W_packed must have K/4 columns")
+    _need(y, torch.float32, "y", shape=(M, N))
+    _check(lib().bitlinear_forward_f32_noalloc(_ptr(X), M, K, _ptr(gain), float(eps), act, _ptr(W_packed), _ptr(gamma),
+                                               N, _ptr(y), int(bool(residual)), _stream(stream)),
+           "bitlinear_forward_f32_noalloc")
     return y
 
 

@@ -601,6 +601,32 @@ void launch_attn(const bl::AttnArgs& a, int M, hipStream_t stream)
     hipLaunchKernelGGL((bl::attn_chunk_kernel<GB, LOOP>), grid, dim3(256), 0, stream, a);
 }
 
+// Fixed scratch of the no-allocation fused call: one copy in each device's memory, held
+// until the process ends. Host code never passes this name to a kernel or a copy (on the
+// host it only stands in for the symbol); it uses the device address looked up below.
+constexpr size_t kNoAllocScratchBytes = BITLINEAR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up with that device current
+// on the first call there and kept per device (each device holds its own copy at its own
+// address). Null when the lookup fails.
+void* scratch_address()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q)
+            return nullptr;
+        g_scratch_addr[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -612,7 +638,9 @@ const char* bitlinear_status_string(int status)
     case BITLINEAR_ERR_NULL: return "a required pointer is NULL";
     case BITLINEAR_ERR_SHAPE: return "a size is out of range or K is not a multiple of 4";
     case BITLINEAR_ERR_ALIGN: return "a pointer is not aligned as required";
-    case BITLINEAR_ERR_WORKSPACE: return "workspace is smaller than bitlinear_pack_workspace_bytes";
+    case BITLINEAR_ERR_WORKSPACE:
+        return "the workspace is smaller than the call's *_workspace_bytes (for the no-allocation call: the sizes "
+               "need more than its fixed scratch)";
     case BITLINEAR_ERR_ALIAS: return "an output buffer overlaps an input buffer";
     case BITLINEAR_ERR_HIP: return "the HIP runtime rejected a launch";
     default: return "unknown status";
@@ -795,6 +823,27 @@ int bitlinear_forward_f32_ws(const float* X, int64_t M, int64_t K, const float* 
     if ((st = bitlinear_quantize_act(X, M, K, gain, eps, act, xq, xs, stream)) != BITLINEAR_OK)
         return st;
     return forward_impl(xq, xs, M, K, W_packed, gamma, N, Y, nullptr, residual ? 1 : 0, stream, part);
+}
+
+int bitlinear_forward_f32_noalloc(const float* X, int64_t M, int64_t K, const float* gain, float eps, int act,
+                                  const uint8_t* W_packed, const float* gamma, int64_t N, float* Y, int residual,
+                                  hipStream_t stream)
+{
+    int st = check_f32_args(X, M, K, gain, act, W_packed, gamma, N, Y);
+    if (st != BITLINEAR_OK)
+        return st;
+    const size_t need = bitlinear_forward_f32_workspace_bytes(M, N, K);
+    if (need == 0)
+        return forward_f32_impl(X, M, K, gain, eps, act, W_packed, gamma, N, Y, residual ? 1 : 0, stream);
+    if (need > kNoAllocScratchBytes)
+        return BITLINEAR_ERR_WORKSPACE;
+    void* ws = scratch_address();
+    if (!ws)
+        return BITLINEAR_ERR_HIP;
+    // the codes, scales and split partials are written before they are read, so the
+    // scratch needs no clearing
+    return bitlinear_forward_f32_ws(X, M, K, gain, eps, act, W_packed, gamma, N, Y, residual, ws,
+                                    kNoAllocScratchBytes, stream);
 }
 
 int64_t bitlinear_packed5_row_bytes(int64_t K)

@@ -149,6 +149,26 @@ def test_forward_f32_ws_rejects_before_launch(L):
     assert g == ERR_SHAPE
 
 
+def test_forward_f32_noalloc_rejects_before_launch(L):
+    """The no-allocation call checks its arguments like the workspace call, and rejects
+    sizes that need more than its fixed scratch (the header's limit) before any HIP call."""
+    m = re.search(r"#define BITLINEAR_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == bl.NOALLOC_SCRATCH_BYTES
+    a = 1 << 40
+    f = L.bitlinear_forward_f32_noalloc
+    args = lambda **kw: [kw.get("X", P(a)), kw.get("M", 64), kw.get("K", 2560), kw.get("g", None), 1e-5,
+                         kw.get("act", 0), kw.get("W", P(2 * a)), kw.get("gm", P(3 * a)), kw.get("N", 256),
+                         kw.get("Y", P(4 * a)), 0, None]
+    assert f(*args(X=None)) == ERR_NULL
+    assert f(*args(K=2562)) == ERR_SHAPE
+    assert f(*args(act=3)) == ERR_SHAPE
+    assert f(*args(X=P(a + 4))) == ERR_ALIGN
+    assert f(*args(Y=P(2 * a))) == ERR_ALIAS
+    # 4096 tokens x 16384: 64 MiB of codes, more than the scratch
+    assert f(*args(M=4096, K=16384, N=64)) == ERR_WORKSPACE
+    assert bl.bitlinear_forward_f32_workspace_bytes(2048, 28672, 8192) <= bl.NOALLOC_SCRATCH_BYTES
+
+
 def test_forward_ws_rejects_before_launch(L):
     f = L.bitlinear_forward_ws
     a = 1 << 26
