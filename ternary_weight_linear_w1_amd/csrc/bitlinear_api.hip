@@ -94,7 +94,7 @@ int64_t sum_levels(int64_t n, int64_t* sizes, int max_levels, int* nlev)
 
 // Launch shapes were chosen by timing back-to-back launches on MI355X for the BitNet
 // 2B (K = 2560, 6912) and 100B (K = 8192, 28672) layer shapes.
-template <int L, int MT, int CPL, int R, bool FUSED>
+template <int L, int MT, int CPL, int R, bool FUSED, int S = 2>
 void launch_k64(const bl::FwdArgs& a, int wg_per_cu, hipStream_t stream)
 {
     constexpr int RPP = (256 / L) * R;
@@ -111,42 +111,55 @@ void launch_k64(const bl::FwdArgs& a, int wg_per_cu, hipStream_t stream)
     if (a.residual) {
         // (the row loop strides by the grid, so any grid width is correct)
         if constexpr (MT * R <= 4)
-            hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, R, FUSED, true>), dim3(gx, gy), dim3(256), lds, stream,
+            hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, R, FUSED, true, S>), dim3(gx, gy), dim3(256), lds, stream,
                                a);
         else
-            hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, 1, FUSED, true>), dim3(gx, gy), dim3(256), lds, stream,
+            hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, 1, FUSED, true, S>), dim3(gx, gy), dim3(256), lds, stream,
                                a);
     } else
-        hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, R, FUSED, false>), dim3(gx, gy), dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, R, FUSED, false, S>), dim3(gx, gy), dim3(256), lds, stream, a);
 }
 
-// One token per tile: up to 4 chunks (256 codes) per lane.
+// One token per tile: up to 4 chunks (256 codes) per lane (7 for the longest rows).
+// Launch shapes (lanes per row L, chunks per lane, rows per lane, passes in flight S,
+// blocks per CU) from graph-timed sweeps on MI355X over the BitNet 2B and 100B shapes;
+// a third pass in flight pays where a block holds few rows per pass or has a long fused
+// prologue to hide (100B down: 20.3 -> 18.8 us fused; 100B O product: 5.8 -> 5.3 us).
 template <bool FUSED>
 bool dispatch_mt1(const bl::FwdArgs& a, hipStream_t stream)
 {
     const int KC = a.K / 64;
-    const bool big = a.N * (int64_t)a.K >= (int64_t(64) << 20);   // >= 16 MB of packed weights
+    const int64_t nk = a.N * (int64_t)a.K;
+    const bool big = nk >= (int64_t(64) << 20);   // >= 16 MB of packed weights
     if (KC <= 48) {
-        // fused, 2B-sized rows: shorter matrices take 32 lanes x 2 chunks (more blocks),
-        // longer ones two rows per lane (graph-timed on the 2B layer)
-        if constexpr (FUSED) {
-            if (a.N <= 4096)
-                launch_k64<32, 1, 2, 1, FUSED>(a, 1, stream);
+        // 2B-sized rows: 16 lanes x 3 chunks, two rows per lane for the longer matrices
+        if (a.N <= 4096) {
+            if constexpr (FUSED)
+                launch_k64<16, 1, 3, 1, FUSED>(a, 1, stream);
             else
-                launch_k64<16, 1, 3, 2, FUSED>(a, 1, stream);
+                launch_k64<16, 1, 3, 1, FUSED>(a, 2, stream);
         } else {
-            launch_k64<16, 1, 3, 1, FUSED>(a, 2, stream);
+            launch_k64<16, 1, 3, 2, FUSED>(a, 1, stream);
         }
         return true;
     }
     if (KC <= 64) { launch_k64<16, 1, 4, 1, FUSED>(a, 2, stream); return true; }
     if (KC <= 128) {
-        if (!big)
-            launch_k64<32, 1, 4, 1, FUSED>(a, 1, stream);
-        else if constexpr (FUSED)  // two blocks per CU from ~20 MB of packed weights (100B QKV, up)
-            launch_k64<32, 1, 4, 1, FUSED>(a, a.N * (int64_t)a.K >= (int64_t(72) << 20) ? 2 : 1, stream);
-        else  // one row per lane and more blocks keep the HBM queue fuller on long matrices
-            launch_k64<32, 1, 4, 1, FUSED>(a, a.N * (int64_t)a.K >= (int64_t(128) << 20) ? 3 : 2, stream);
+        if (!big) {   // 2B down projection (K = 6912): a wave per row
+            if constexpr (FUSED)
+                launch_k64<64, 1, 2, 1, FUSED, 3>(a, 1, stream);
+            else
+                launch_k64<64, 1, 2, 1, FUSED>(a, 2, stream);
+        } else if (nk < (int64_t(72) << 20)) {   // 100B O (K = N = 8192)
+            if constexpr (FUSED)
+                launch_k64<32, 1, 4, 1, FUSED, 3>(a, 1, stream);
+            else
+                launch_k64<64, 1, 2, 1, FUSED, 3>(a, 3, stream);
+        } else if constexpr (FUSED) {   // two blocks per CU from ~20 MB of packed weights (100B QKV, up)
+            launch_k64<32, 1, 4, 1, FUSED>(a, 2, stream);
+        } else {   // one row per lane and more blocks keep the HBM queue fuller on long matrices
+            launch_k64<32, 1, 4, 1, FUSED>(a, nk >= (int64_t(128) << 20) ? 3 : 2, stream);
+        }
         return true;
     }
     if (KC <= 256) {  // the fused prologue keeps the whole row in registers: one block per CU
@@ -154,12 +167,16 @@ bool dispatch_mt1(const bl::FwdArgs& a, hipStream_t stream)
         return true;
     }
     if (KC <= 512) {
-        if constexpr (FUSED)
+        if (KC <= 448) {   // one wave per row (no cross-wave sum), 7 chunks per lane: 100B down
+            if constexpr (FUSED)
+                launch_k64<64, 1, 7, 1, FUSED, 3>(a, 1, stream);
+            else
+                launch_k64<64, 1, 7, 1, FUSED>(a, 1, stream);
+        } else if constexpr (FUSED) {
             launch_k64<128, 1, 4, 1, FUSED>(a, 1, stream);
-        else if (KC <= 448)  // one wave per row (no cross-wave sum), 7 chunks per lane: 100B down
-            launch_k64<64, 1, 7, 1, FUSED>(a, 1, stream);
-        else
+        } else {
             launch_k64<256, 1, 2, 2, FUSED>(a, 3, stream);  // codes straight to registers
+        }
         return true;
     }
     if (KC <= 1024) { launch_k64<256, 1, 4, 1, FUSED>(a, FUSED ? 1 : 2, stream); return true; }

@@ -430,9 +430,10 @@ __device__ __forceinline__ int group_sum(int v)
 // LDS when many row groups share them (L < 64); with L >= 64 (at most four row groups)
 // each lane loads its own chunks into registers ahead of its weights, which skips the
 // staging and its barriers.
-template <int L, int MT, int CPL, int R, bool FUSED, bool RES>
+template <int L, int MT, int CPL, int R, bool FUSED, bool RES, int S = 2>
 __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
 {
+    static_assert(S >= 2 && S <= 8, "passes in flight");
     constexpr int NT = 256;
     static_assert(CPL * MT <= 8, "activation codes must fit in 128 VGPRs");
     constexpr int RG = NT / L;             // row groups per block
@@ -537,10 +538,11 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
         const float gamma = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(
                        __builtin_amdgcn_make_buffer_rsrc((void*)a.gamma, (short)0, 4, kBufFlags), 0, 0, 0));
-        u32x4 cur[R][CPL], nxt[R][CPL];
-        float ycur[R][MT], ynxt[R][MT];
-        load_pass(rb, cur, ycur, ry, mt);
-        load_pass(rb + pstride, nxt, ynxt, ry, mt);
+        u32x4 wbuf[S][R][CPL];
+        float ybuf[S][R][MT];
+#pragma unroll
+        for (int p = 0; p < S; ++p)
+            load_pass(rb + p * pstride, wbuf[p], ybuf[p], ry, mt);
 
         float s[MT];
         if constexpr (DIRECT) {
@@ -693,15 +695,33 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
             }
         };
 
-        // Two named buffers in turn (no register copy at the loop edge), so each wait
-        // for weight data sits right before its use; two passes are in flight.
-        for (; rb < N; rb += 2 * pstride) {
-            compute_pass(rb, cur, ycur);
-            load_pass(rb + 2 * pstride, cur, ycur, ry, mt);
-            if (rb + pstride >= N)
+        // S named buffers in turn (no register copy at the loop edge), so each wait for
+        // weight data sits right before its use; S passes are in flight.
+        if constexpr (S == 2) {
+            for (; rb < N; rb += 2 * pstride) {
+                compute_pass(rb, wbuf[0], ybuf[0]);
+                load_pass(rb + 2 * pstride, wbuf[0], ybuf[0], ry, mt);
+                if (rb + pstride >= N)
+                    break;
+                compute_pass(rb + pstride, wbuf[1], ybuf[1]);
+                load_pass(rb + 3 * pstride, wbuf[1], ybuf[1], ry, mt);
+            }
+        } else
+        for (; rb < N; rb += S * pstride) {
+            bool done = false;
+#pragma unroll
+            for (int p = 0; p < S; ++p) {
+                if (!done) {
+                    if (p > 0 && rb + p * pstride >= N) {
+                        done = true;
+                    } else {
+                        compute_pass(rb + p * pstride, wbuf[p], ybuf[p]);
+                        load_pass(rb + (p + S) * pstride, wbuf[p], ybuf[p], ry, mt);
+                    }
+                }
+            }
+            if (done)
                 break;
-            compute_pass(rb + pstride, nxt, ynxt);
-            load_pass(rb + 3 * pstride, nxt, ynxt, ry, mt);
         }
         tile += gridDim.y;
     } while (tile < ntiles);
