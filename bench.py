@@ -131,9 +131,12 @@ class Mat:
         self.y = torch.empty((M, N), dtype=torch.float32, device=dev)
         self.xq = torch.empty((M, K), dtype=torch.int8, device=dev)
         self.s = torch.empty((M,), dtype=torch.float32, device=dev)
+        need = bl.bitlinear_forward_f32_workspace_bytes(M, N, K)
+        self.ws = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
 
     def fused(self, bl, c):
-        bl.bitlinear_forward_f32(self.x, self.copies[c], self.gamma, self.gain, EPS, self.relu2, y=self.y)
+        bl.bitlinear_forward_f32(self.x, self.copies[c], self.gamma, self.gain, EPS, self.relu2, y=self.y,
+                                 workspace=self.ws)
 
     def prequant(self, bl):
         bl.bitlinear_quantize_act(self.x, self.gain, EPS, self.relu2, xq=self.xq, scale=self.s)
@@ -563,7 +566,8 @@ def run_headline(torch, bl, datagen, dev, steps, warmup):
         clones = [mats[0][i].copies[0].clone() for _ in range(extra_c)]
         m0 = mats[0][i]
         rot = [lambda m=m, c=c: m.fused(bl, c) for m, c in inst] + \
-              [lambda w=w: bl.bitlinear_forward_f32(m0.x, w, m0.gamma, m0.gain, EPS, m0.relu2, y=m0.y) for w in clones]
+              [lambda w=w: bl.bitlinear_forward_f32(m0.x, w, m0.gamma, m0.gain, EPS, m0.relu2, y=m0.y, workspace=m0.ws)
+               for w in clones]
         a = time_kernel(torch, lambda j: rot[j](), len(rot), 200)
         b = m0.bytes()
         per[name] = {"us": round(a * 1e6, 3), "GB/s": round(b / a / 1e9, 1), "frac_hbm": round(b / a / 1e9 / HBM_PEAK_GBS, 4),
