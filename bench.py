@@ -35,6 +35,8 @@ Also printed in the same JSON line:
 Other modes:
   --profile roofline   only the dominant kernel plus a copy kernel of known size
                        (for rocprofv3 --pmc runs);
+  --profile prefill    the same for the prefill figure's roofline kernel (the down
+                       projection's GEMM at M = 2048);
   --summarize-pmc F W  turn two rocprofv3 counter CSVs into profiles/ text;
   --summarize-trace T S OUT  turn a rocprofv3 kernel trace and its stats CSV into a
                        profiles/ text (per kernel and grid: calls, average, median, min).
@@ -75,6 +77,7 @@ LAYER_100B_TP8 = [("qkv", 1280, 8192, "plain"), ("o", 8192, 1024, "norm"), ("up"
                   ("down", 8192, 3584, "relu2norm")]
 
 SLICE_LAYERS = 4
+PREFILL_M = 2048
 DOMINANT = "down"      # the longest launch of the headline step: 100B down projection, M = 1
 # What decides the measured GEMV's traffic: its kernel, the shared device helpers, and the
 # GEMV launch-shape section of the API file (from its "forward dispatch" banner to the MFMA
@@ -85,12 +88,22 @@ DISPATCH_SRC = ("ternary_weight_linear_w1_amd/csrc/bitlinear_api.hip", "forward 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_down_100B_M1_traffic.txt")
 
 
-def kernel_hash() -> str:
+# The same for the prefill figure's roofline kernel (the down projection's GEMM at M = 2048):
+# the GEMM kernel, the shared helpers, and the GEMM tile choice in the API file.
+PREFILL_DOMINANT = "down"
+KERNEL_SRC_PREFILL = ["ternary_weight_linear_w1_amd/csrc/gemm.hpp", "ternary_weight_linear_w1_amd/csrc/device_common.hpp"]
+DISPATCH_SRC_PREFILL = ("ternary_weight_linear_w1_amd/csrc/bitlinear_api.hip", "// Many tokens: int8 MFMA GEMM",
+                        "// Few tokens on the matrix cores")
+TRAFFIC_FILE_PREFILL = os.path.join(ROOT, "profiles", "gemm_down_2B_M2048_traffic.txt")
+
+
+def kernel_hash(target="decode") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SRC:
+    srcs, (path, start, end) = ((KERNEL_SRC, DISPATCH_SRC) if target == "decode"
+                                else (KERNEL_SRC_PREFILL, DISPATCH_SRC_PREFILL))
+    for p in srcs:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
-    path, start, end = DISPATCH_SRC
     with open(os.path.join(ROOT, path), "rb") as f:
         text = f.read()
     i = text.index(start.encode())
@@ -268,15 +281,16 @@ def cpu_baseline(torch, mats, seconds=8.0):
 
 # ----------------------------------------------------------------------------- traffic
 
-def read_traffic():
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(target="decode"):
+    path = TRAFFIC_FILE if target == "decode" else TRAFFIC_FILE_PREFILL
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_hash(target):
         return None
     try:
         return int(float(vals["traffic_bytes_per_launch"]))
@@ -323,7 +337,7 @@ def summarize_trace(trace_csv, stats_csv, out, command="--steps 80 --warmup 8 --
     log("wrote %s" % out)
 
 
-def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
+def summarize_pmc(fetch_csv, write_csv, copy_bytes, out, target="decode"):
     import csv
 
     def per_kernel(path, counter):
@@ -339,7 +353,7 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
     wr = per_kernel(write_csv, "WRITE_SIZE")
     # the measured kernel: the library kernel launched most often (200 times in --profile
     # roofline; the packing kernels of the setup run a few times)
-    lib_k = [k for k in fe if "bl::" in k]
+    lib_k = [k for k in fe if "bl::" in k and ("gemm" in k) == (target == "prefill")]
     gk = [max(lib_k, key=lambda k: len(fe[k]))] if lib_k else []
     ck = [k for k in fe if "copy" in k.lower()]
     if len(gk) != 1 or not ck:
@@ -353,19 +367,27 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
     g_write_kib = sum(wr[gk[0]]) / len(wr[gk[0]])
     g_fetch = g_fetch_kib * 1024.0 * f_factor
     g_write = g_write_kib * 1024.0 * w_factor
-    N, K, mode = [(n, k, m) for (nm, n, k, m) in LAYER_100B if nm == DOMINANT][0]
-    alg = layer_bytes(N, K, 1, mode)
+    if target == "decode":
+        N, K, mode = [(n, k, m) for (nm, n, k, m) in LAYER_100B if nm == DOMINANT][0]
+        alg = layer_bytes(N, K, 1, mode)
+        title = "the down-projection product (100B slice, %d->%d, M=1, fused ReLU^2+subln input)" % (K, N)
+    else:
+        N, K, mode = [(n, k, m) for (nm, n, k, m) in LAYER_2B if nm == PREFILL_DOMINANT][0]
+        alg = layer_bytes(N, K, PREFILL_M, mode, fused=False)
+        title = ("the down-projection GEMM (2B layer, %d->%d, M=%d, pre-quantized int8 activations)"
+                 % (K, N, PREFILL_M))
     with open(out, "w") as f:
-        f.write("# HBM traffic of the down-projection product (100B slice, %d->%d, M=1, fused ReLU^2+subln input)\n"
-                % (K, N))
+        f.write("# HBM traffic of %s\n" % title)
         f.write("# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by\n")
         f.write("# the same counter read for a plain copy kernel of %d bytes read and written.\n" % copy_bytes)
         f.write("# commands:\n")
+        prof = "roofline" if target == "decode" else "prefill"
         f.write("#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch --output-format csv -- "
-                "python3 bench.py --profile roofline\n")
+                "python3 bench.py --profile %s\n" % prof)
         f.write("#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write --output-format csv -- "
-                "python3 bench.py --profile roofline\n")
-        f.write("#   python3 bench.py --summarize-pmc <fetch csv> <write csv>\n")
+                "python3 bench.py --profile %s\n" % prof)
+        f.write("#   python3 bench.py --summarize-pmc <fetch csv> <write csv>%s\n"
+                % ("" if target == "decode" else " --pmc-target prefill"))
         f.write("gemv_kernel = %s\n" % gk[0])
         f.write("copy_kernel = %s\n" % copyk)
         f.write("copy_fetch_kib = %.1f\ncopy_write_kib = %.1f\n" % (copy_fetch_kib, copy_write_kib))
@@ -374,7 +396,7 @@ def summarize_pmc(fetch_csv, write_csv, copy_bytes, out):
         f.write("gemv_fetch_bytes = %d\ngemv_write_bytes = %d\n" % (g_fetch, g_write))
         f.write("algorithmic_bytes_per_launch = %d\n" % alg)
         f.write("traffic_bytes_per_launch = %d\n" % (g_fetch + g_write))
-        f.write("kernel_source_sha256_16 = %s\n" % kernel_hash())
+        f.write("kernel_source_sha256_16 = %s\n" % kernel_hash(target))
     print(open(out).read())
 
 
@@ -385,7 +407,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--profile", choices=["none", "roofline"], default="none")
+    ap.add_argument("--profile", choices=["none", "roofline", "prefill"], default="none")
+    ap.add_argument("--pmc-target", choices=["decode", "prefill"], default="decode",
+                    help="which kernel --summarize-pmc summarizes")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary configurations")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only the decode-attention cases (a short program for kernel traces)")
@@ -413,7 +437,8 @@ def main():
         summarize_mfma(*args.summarize_mfma)
         return 0
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_bytes, TRAFFIC_FILE)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_bytes,
+                      TRAFFIC_FILE if args.pmc_target == "decode" else TRAFFIC_FILE_PREFILL, args.pmc_target)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the W1.58A8 BitLinear path here is a single-GPU build "
@@ -461,6 +486,21 @@ def main():
         print(json.dumps({"profile": "roofline", "kernel_launches": 200, "copy_bytes": args.copy_bytes}))
         return 0
 
+    if args.profile == "prefill":
+        i, (name, N, K, mode) = [(i, sp) for i, sp in enumerate(LAYER_2B) if sp[0] == PREFILL_DOMINANT][0]
+        m = Mat(torch, bl, datagen, 4, i + 4, name, N, K, mode, PREFILL_M, 2, dev)
+        m.x = datagen.heavy_channel_acts_torch(PREFILL_M, K, datagen.stream_id(4, 1, i, 1), dev)
+        m.prequant(bl)
+        for j in range(50):
+            m.forward(bl, j % 2)
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "prefill", "kernel_launches": 50, "copy_bytes": args.copy_bytes}))
+        return 0
+
     head = run_headline(torch, bl, datagen, dev, args.steps, args.warmup)
     slice_mats = head.pop("_mats")
     roofline = head.pop("_roofline")
@@ -474,7 +514,7 @@ def main():
     del slice_mats
     torch.cuda.empty_cache()
 
-    prefill = run_prefill_headline(torch, bl, datagen, dev, 2048, args.steps, args.warmup)
+    prefill = run_prefill_headline(torch, bl, datagen, dev, PREFILL_M, args.steps, args.warmup)
     torch.cuda.empty_cache()
 
     if not args.no_extra:
@@ -495,9 +535,12 @@ def main():
 
 
 def graph_of(torch, fn):
+    """A captured graph, replayed once (its first launch uploads it) before it is timed."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fn()
+    g.replay()
+    torch.cuda.synchronize()
     return g
 
 
@@ -546,18 +589,9 @@ def run_headline(torch, bl, datagen, dev, steps, warmup):
     torch.cuda.synchronize()
     pair = [graph_of(torch, lambda: (step(0), step(1))), graph_of(torch, lambda: (step(1), step(0)))]
     single = [graph_of(torch, lambda: step(0)), graph_of(torch, lambda: step(1))]
-    log("warmup %d steps" % warmup)
-    timed_replays(torch, rotation_plan(pair, single, 0, warmup))
-    log("timing %d steps" % steps)
-    gpu_s, wall = timed_replays(torch, rotation_plan(pair, single, warmup % 2, steps))
-    value = step_bytes * steps / gpu_s / 1e9
-    ms_per_step = gpu_s / steps * 1e3
-    log("value %.1f GB/s (%.4f ms/step by events; %.4f ms/step by host wall clock)" %
-        (value, ms_per_step, wall / steps * 1e3))
-    del pair, single
-
     # per-matrix launches of the step (fused entry), each over >= 1 GiB of rotating weights:
-    # the slice's 8 instances of the matrix (4 layers x 2 copies) plus clones
+    # the slice's 8 instances of the matrix (4 layers x 2 copies) plus clones; timed before the
+    # steps, which then run on a GPU that is already busy (clocks up)
     per = {}
     dom_avg = None
     for i, (name, N, K, mode) in enumerate(LAYER_100B):
@@ -576,6 +610,16 @@ def run_headline(torch, bl, datagen, dev, steps, warmup):
             dom_avg, dom_bytes = a, b
         del clones, rot
         torch.cuda.empty_cache()
+    log("warmup %d steps" % warmup)
+    timed_replays(torch, rotation_plan(pair, single, 0, warmup))
+    log("timing %d steps" % steps)
+    gpu_s, wall = timed_replays(torch, rotation_plan(pair, single, warmup % 2, steps))
+    value = step_bytes * steps / gpu_s / 1e9
+    ms_per_step = gpu_s / steps * 1e3
+    log("value %.1f GB/s (%.4f ms/step by events; %.4f ms/step by host wall clock)" %
+        (value, ms_per_step, wall / steps * 1e3))
+    del pair, single
+
     log("slice per-matrix (fused, M=1): %s" % per)
     achieved = dom_bytes / dom_avg / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -624,17 +668,19 @@ def run_prefill_headline(torch, bl, datagen, dev, M, steps, warmup):
     torch.cuda.synchronize()
     pair = [graph_of(torch, lambda: (step(0), step(1))), graph_of(torch, lambda: (step(1), step(0)))]
     single = [graph_of(torch, lambda: step(0)), graph_of(torch, lambda: step(1))]
+    # per-matrix launches first: graphs of 100 launches each, about 40 ms of load, after which
+    # the clocks have settled (a cold GPU runs the first ~60 steps up to 15% slower)
+    per = {}
+    for m in mats:
+        a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), 2, 100)
+        o = 2.0 * M * m.N * m.K
+        per[m.name] = {"us": round(a * 1e6, 2), "TOPS": round(o / a / 1e12, 1),
+                       "frac_int8_peak": round(o / a / 1e12 / INT8_PEAK_TOPS, 4)}
     timed_replays(torch, rotation_plan(pair, single, 0, warmup))
     gpu_s, wall = timed_replays(torch, rotation_plan(pair, single, warmup % 2, steps))
     tops = ops * steps / gpu_s / 1e12
     del pair, single
-    per = {}
-    for m in mats:
-        a = time_kernel(torch, lambda c, m=m: m.forward(bl, c), 2, 20)
-        o = 2.0 * M * m.N * m.K
-        per[m.name] = {"us": round(a * 1e6, 2), "TOPS": round(o / a / 1e12, 1),
-                       "frac_int8_peak": round(o / a / 1e12 / INT8_PEAK_TOPS, 4)}
-    dom = max(per, key=lambda k: per[k]["us"])
+    dom = PREFILL_DOMINANT   # the longest GEMM of the step on the boxes measured (down, with up close)
     dm = [m for m in mats if m.name == dom][0]
     a = per[dom]["us"] * 1e-6
     achieved = 2.0 * M * dm.N * dm.K / a / 1e12
@@ -648,10 +694,11 @@ def run_prefill_headline(torch, bl, datagen, dev, M, steps, warmup):
                       "timing": "HIP events around graph replays captured before timing; %.4f ms/step by host "
                                 "wall clock" % (wall / steps * 1e3)},
            "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-                        "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                        "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": read_traffic("prefill"),
+                        "algorithmic_bytes": layer_bytes(dm.N, dm.K, M, dm.mode, fused=False),
                         "kernel": "bitlinear_forward %s %d->%d, M=%d (int8 matrix-core GEMM)" % (dom, dm.K, dm.N, M),
                         "avg_us": per[dom]["us"],
-                        "timing": "HIP events around a graph of 20 back-to-back launches (two weight copies)"},
+                        "timing": "HIP events around a graph of 100 back-to-back launches (two weight copies)"},
            "per_matrix": per}
     log("prefill M=%d: %.1f TOPS (%.4f ms/step); per matrix %s" % (M, tops, gpu_s / steps * 1e3, per))
     del mats
