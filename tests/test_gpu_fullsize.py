@@ -89,10 +89,11 @@ def check_matrix(cfg, idx, N, K, mode, M, fused, heavy=False, sampled=False):
 @pytest.mark.parametrize("M", [1, 4, 8])
 @pytest.mark.parametrize("i", range(4))
 def test_2b_layer_decode(M, i):
+    """Both entries at every token count: the fused call and the product on pre-quantized
+    codes (at one token the two take different launch shapes)."""
     name, N, K, mode = LAYER_2B[i]
     check_matrix(2, i + 10 * M, N, K, mode, M, fused=(M == 1))
-    if M > 1:
-        check_matrix(2, i + 10 * M + 100, N, K, mode, M, fused=True)
+    check_matrix(2, i + 10 * M + 100, N, K, mode, M, fused=(M != 1))
 
 
 @pytest.mark.parametrize("M", [512, 2048])

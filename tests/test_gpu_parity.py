@@ -361,6 +361,9 @@ RESIDUAL_CASES = [
     (1, 2560, 2560, "norm"), (1, 2560, 6912, "relu2norm"), (1, 300, 6912, "gatednorm"), (2, 70, 2560, None),
     (4, 129, 8192, None), (3, 6912, 6912, None), (1, 37, 260, "norm"), (5, 33, 260, None), (64, 200, 2560, None),
     (16, 33, 64, None), (1, 1024, 28672, None),
+    # one-token launch shapes of the decode stack and the 100B slice: two rows per lane
+    # (2B up), three passes in flight (100B O: both the fused and the pre-quantized shape)
+    (1, 6912, 2560, None), (1, 8192, 8192, "norm"),
 ]
 
 
