@@ -143,3 +143,52 @@ def test_100b_tp8_shard_m1(i):
     name, N, K, mode = LAYER_100B_TP8[i]
     check_matrix(6, i, N, K, mode, 1, fused=True)
     check_matrix(6, i + 4, N, K, mode, 1, fused=False)
+
+
+def test_max_output_width_four_token_tiles():
+    """The widest output the chunked product takes, N = 2^27 - 1 rows, with four-token tiles
+    (M = 4, K = 64): a tile's output buffer is then 4 N floats = 2^31 - 16 bytes, ending
+    exactly at the out-of-range offset that masked lanes store to, so those stores must be
+    dropped and every output row, the last ones included, must hold the oracle's values.
+    Checked on sampled rows and on the last 64 rows of every token."""
+    M, N, K = 4, (1 << 27) - 1, 64
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(2027)
+    codes = torch.randint(0, 3, (N, K // 4, 4), generator=gen, device=DEV, dtype=torch.int32)
+    packed = (codes[..., 0] | (codes[..., 1] << 2) | (codes[..., 2] << 4) | (codes[..., 3] << 6)).to(torch.uint8)
+    del codes
+    gamma = torch.tensor([0.0123], dtype=torch.float32, device=DEV)
+    x = datagen.outlier_acts(M, K, 2028)
+    xq, s = bl.bitlinear_quantize_act(torch.from_numpy(x).to(DEV))
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    bl.bitlinear_forward(xq, s, packed, gamma, y=y, split=False)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(N, seed=5), np.arange(N - 64, N)]))
+    q, bad = oracle.unpack(packed[torch.from_numpy(rows).to(DEV)].cpu().numpy(), K)
+    assert bad == 0
+    oxq, os_ = oracle.quantize_act(x)
+    assert np.array_equal(xq.cpu().numpy(), oxq)
+    _, oy = oracle.forward(oxq, os_, q, np.float32(0.0123))
+    yh = y[:, torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    assert np.array_equal(yh.view(np.int32), oy.view(np.int32))
+
+
+def test_max_k_one_and_two_tokens():
+    """K at the API maximum (2^20): the product on the generic path, plain and subln input,
+    full outputs against the oracle."""
+    K = 1 << 20
+    for M, N, mode in ((1, 3, None), (2, 5, "norm")):
+        w = datagen.gg_weights(N, K, 2030 + M)
+        x = datagen.outlier_acts(M, K, 2031 + M)
+        gain = datagen.gains(K, 2032) if mode else None
+        packed, gamma = bl.bitlinear_pack_weights(torch.from_numpy(w).to(DEV))
+        y = bl.bitlinear_forward_f32(torch.from_numpy(x).to(DEV), packed, gamma,
+                                     None if gain is None else torch.from_numpy(gain).to(DEV), EPS, 0)
+        torch.cuda.synchronize()
+        o = oracle.bitlinear(x, w, gain=gain, eps=EPS) if mode else oracle.bitlinear(x, w)
+        assert np.array_equal(packed.cpu().numpy(), o["packed"])
+        yh = y.cpu().numpy()
+        if mode is None:
+            assert np.array_equal(yh.view(np.int32), o["y"].view(np.int32))
+        else:
+            assert (np.abs(yh.astype(np.float64) - o["y"]) <= 1e-6 * np.abs(o["y"].astype(np.float64))).all()

@@ -105,3 +105,35 @@ def test_no_alloc_rejects_sizes_beyond_its_scratch():
     torch.cuda.synchronize()
     assert st == ERR_WORKSPACE
     assert bool((y == 7.0).all())             # nothing was enqueued
+
+
+def test_no_alloc_inside_a_captured_graph():
+    """The use the entry point is for: after a first call outside capture (which looks up
+    the device's scratch address), calls captured in a graph allocate nothing and every
+    replay, with eager work between replays, gives the workspace call's bits."""
+    c1 = case(64, 2560, 6912, "relu2norm", seed=900)
+    c2 = case(12, 8192, 28672, "plain", seed=901)      # K split: partials in the scratch
+    ref1, _ = with_workspace(c1, False)
+    ref2, _ = with_workspace(c2, False)
+    y1 = torch.empty_like(ref1)
+    y2 = torch.empty_like(ref2)
+    assert no_alloc(c1, False, y1) == 0                 # outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            st = ctypes.c_void_p(side.cuda_stream)
+            r1 = bl.lib().bitlinear_forward_f32_noalloc(P(c1["x"]), c1["M"], c1["K"], P(c1["gain"]), EPS, c1["act"],
+                                                         P(c1["packed"]), P(c1["gamma"]), c1["N"], P(y1), 0, st)
+            r2 = bl.lib().bitlinear_forward_f32_noalloc(P(c2["x"]), c2["M"], c2["K"], P(c2["gain"]), EPS, c2["act"],
+                                                         P(c2["packed"]), P(c2["gamma"]), c2["N"], P(y2), 0, st)
+    assert r1 == 0 and r2 == 0
+    for _ in range(3):
+        y1.fill_(float("nan"))
+        y2.fill_(float("nan"))
+        with_workspace(c2, False)                       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y1, ref1) and torch.equal(y2, ref2)
