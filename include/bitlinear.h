@@ -289,8 +289,8 @@ int bitlinear_forward5(const int8_t* Xq, const float* x_scale, int64_t M, int64_
  * Requirements: head_dim == 128; heads a multiple of kv_heads, heads <= 4096;
  * 1 <= M <= 65535; 1 <= capacity <= BITLINEAR_MAX_CONTEXT; theta > 0 and finite; every
  * pointer 16-byte aligned (pos 4-byte). No written buffer (caches, out, workspace) may
- * overlap any other argument buffer. Three kernels are enqueued on `stream` (rotate and
- * append; attend over 64-position chunks; merge the chunks).
+ * overlap any other argument buffer. Two kernels are enqueued on `stream` (rotate, append
+ * and attend over 64-position chunks; merge the chunks).
  * bitlinear_attention_workspace_bytes returns 0 for out-of-range sizes.
  */
 size_t bitlinear_attention_workspace_bytes(int64_t M, int64_t heads, int64_t capacity);

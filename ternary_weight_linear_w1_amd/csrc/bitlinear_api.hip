@@ -926,8 +926,8 @@ size_t bitlinear_attention_workspace_bytes(int64_t M, int64_t heads, int64_t cap
 {
     if (M < 1 || heads < 1 || capacity < 1 || M > 65535 || heads > 4096 || capacity > BITLINEAR_MAX_CONTEXT)
         return 0;
-    // chunk partials acc [M][H][S][128], rotated queries [M][H][128], partials (m, l) [M][H][S][2]
-    return (size_t)(M * heads * (attn_chunks(capacity) * (bl::kAttnD + 2) + bl::kAttnD) * 4);
+    // chunk partials acc [M][H][S][128], then partials (m, l) [M][H][S][2]
+    return (size_t)(M * heads * attn_chunks(capacity) * (bl::kAttnD + 2) * 4);
 }
 
 int bitlinear_attention_decode(const float* qkv, uint16_t* k_cache, uint16_t* v_cache, const int32_t* pos,
@@ -958,14 +958,12 @@ int bitlinear_attention_decode(const float* qkv, uint16_t* k_cache, uint16_t* v_
                 return BITLINEAR_ERR_ALIAS;
     const int64_t S = attn_chunks(capacity);
     float* part_acc = static_cast<float*>(workspace);
-    float* qr = part_acc + M * heads * S * bl::kAttnD;
-    float* part_ml = qr + M * heads * bl::kAttnD;
-    // When one 64-position sub-chunk per block needs at most two blocks per compute unit,
-    // the chunk kernel also rotates and appends (no rotate launch). Else each block takes
-    // several sub-chunks (at most 4 query heads per block, which keeps the running state in
-    // registers) so that about four blocks per compute unit remain: measured on MI355X,
-    // three sub-chunks per block beat one (fewer partials to merge) and five or more (each
-    // sub-chunk waits a full memory round trip).
+    float* part_ml = part_acc + M * heads * S * bl::kAttnD;
+    // One 64-position sub-chunk per block while that needs at most two blocks per compute
+    // unit. Else each block walks several sub-chunks (at most 4 query heads per block, which
+    // keeps the running state in registers) so that about three blocks per compute unit
+    // remain: measured on MI355X at 32768 positions, 30.7 us against 32.4 at four blocks
+    // per unit, 34 at two and 34.7 at six.
     const int64_t G = heads / kv_heads;
     const int64_t cus = cu_count();
     const int GB1 = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
@@ -974,17 +972,13 @@ int bitlinear_attention_decode(const float* qkv, uint16_t* k_cache, uint16_t* v_
     int64_t cpb = 1;
     if (loop) {
         GB = GB1 > 4 ? 4 : GB1;
-        cpb = (S * kv_heads * (G / GB) * M + 4 * cus - 1) / (4 * cus);
+        cpb = (S * kv_heads * (G / GB) * M + 3 * cus - 1) / (3 * cus);
     }
     if (kv_heads * (G / GB) > 65535)
         return BITLINEAR_ERR_SHAPE;
-    bl::AttnArgs a{qkv, k_cache, v_cache, pos, out, part_acc, part_ml, qr, (int)heads, (int)kv_heads, (int)capacity,
+    bl::AttnArgs a{qkv, k_cache, v_cache, pos, out, part_acc, part_ml, (int)heads, (int)kv_heads, (int)capacity,
                    (int)S, (int)(cpb < S ? cpb : S), theta};
-    int st = BITLINEAR_OK;
     if (loop) {
-        hipLaunchKernelGGL(bl::attn_rotate_kernel, dim3((unsigned)M), dim3(256), 0, stream, a);
-        if ((st = launched()) != BITLINEAR_OK)
-            return st;
         switch (GB) {
         case 4: launch_attn<4, true>(a, (int)M, stream); break;
         case 2: launch_attn<2, true>(a, (int)M, stream); break;
@@ -998,7 +992,7 @@ int bitlinear_attention_decode(const float* qkv, uint16_t* k_cache, uint16_t* v_
         default: launch_attn<1, false>(a, (int)M, stream); break;
         }
     }
-    st = launched();
+    const int st = launched();
     if (st != BITLINEAR_OK)
         return st;
     hipLaunchKernelGGL(bl::attn_combine_kernel, dim3((unsigned)heads, (unsigned)M), dim3(256), 0, stream, a);

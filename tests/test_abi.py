@@ -267,9 +267,9 @@ def test_five_per_byte_calls_reject_before_launch(L):
 
 def test_attention_workspace_bytes(L):
     # (M, heads, capacity) -> per (sequence, head): ceil(capacity / 64) chunk records of 128 + 2
-    # floats and the 128 rotated query values
+    # floats
     for M, H, C in [(1, 20, 4096), (3, 64, 100), (1, 1, 1), (65535, 1, 64)]:
-        assert bl.bitlinear_attention_workspace_bytes(M, H, C) == M * H * ((-(-C // 64)) * 130 + 128) * 4
+        assert bl.bitlinear_attention_workspace_bytes(M, H, C) == M * H * (-(-C // 64)) * 130 * 4
     for bad in [(0, 20, 64), (1, 0, 64), (1, 20, 0), (65536, 1, 64), (1, 4097, 64), (1, 1, (1 << 24) + 1)]:
         assert bl.bitlinear_attention_workspace_bytes(*bad) == 0
 

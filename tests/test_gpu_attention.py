@@ -85,8 +85,8 @@ CASES = [
     (1, 2, 2, 70, [69]),                 # plain multi-head
     (1, 32, 2, 200, [150]),              # 16 per KV head: two blocks per KV head
     (1, 1, 1, 1, [0]),                   # capacity 1
-    # more blocks than two per compute unit: the rotate launch, then blocks that walk
-    # several 64-position sub-chunks with a running maximum
+    # more blocks than two per compute unit: blocks walk several 64-position sub-chunks
+    # with a running maximum, two sub-chunks' loads in flight
     (1, 20, 5, 32768, [32767]),          # 2B heads, long context
     (8, 20, 5, 4096, [4095, 4000, 3000, 2047, 1024, 700, 64, 5]),   # 8 sequences at mixed positions
     (2, 64, 8, 4096, [4095, 2222]),      # 100B heads: 8 query heads per KV head split in two blocks
@@ -110,17 +110,40 @@ def test_attention_invalid_positions_leave_cache():
     check(3, 8, 2, 200, [200, 57, -1], seed=5)
 
 
-def test_attention_ignores_slots_past_pos():
-    """NaN bit patterns in every slot after pos never reach the output."""
-    M, H, KVH, C, p = 1, 20, 5, 512, 300
+@pytest.mark.parametrize("C,p", [(512, 300), (512, 0), (32768, 20000), (32768, 191)])
+def test_attention_ignores_slots_past_pos(C, p):
+    """NaN bit patterns in slot pos and every slot after it never reach the output (slot
+    pos is overwritten with the new key and value), in the one-sub-chunk form (512) and in
+    the form whose blocks walk several sub-chunks (32768)."""
+    M, H, KVH = 1, 20, 5
     qkv, kc, vc = make(M, H, KVH, C, 6)
-    kc[:, :, p + 1:] = 0x7FC0
-    vc[:, :, p + 1:] = 0x7FC0
+    kc[:, :, p:] = 0x7FC0
+    vc[:, :, p:] = 0x7FC0
+    print("attention NaN past pos: C=%d pos=%d" % (C, p), flush=True)
     out, gkc, gvc = run_gpu(qkv, kc, vc, [p], H, KVH)
     ref, okc, ovc = oracle.attention_decode(qkv, kc, vc, [p], H, KVH, 10000.0)
     assert np.isfinite(out).all()
     assert (gkc == okc).all() and (gvc == ovc).all()
     assert (np.abs(out - ref) <= attention_bound(qkv, okc, ovc, [p], H, KVH)).all()
+
+
+@pytest.mark.parametrize("M,H,KVH,C,pos", [(1, 20, 5, 32768, [100]), (1, 20, 5, 4096, [70]),
+                                           (3, 8, 2, 2000, [1999, 0, 640]), (8, 20, 5, 4096, [4095] + [9] * 7)])
+def test_attention_stale_workspace_is_never_read(M, H, KVH, C, pos):
+    """The merge requests its first batch of chunk records before it has read pos; records
+    past the live ones hold whatever an earlier call left. With every workspace byte 0xFF
+    (NaN floats) beforehand the output still matches the oracle."""
+    qkv, kc, vc = make(M, H, KVH, C, 11)
+    print("attention stale workspace: M=%d H=%d KVH=%d C=%d pos=%s" % (M, H, KVH, C, pos), flush=True)
+    g_qkv = torch.from_numpy(qkv).to(DEV)
+    g_kc = torch.from_numpy(kc.view(np.int16)).to(DEV).view(torch.bfloat16)
+    g_vc = torch.from_numpy(vc.view(np.int16)).to(DEV).view(torch.bfloat16)
+    g_pos = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    ws = torch.full((bl.bitlinear_attention_workspace_bytes(M, H, C),), 0xFF, dtype=torch.uint8, device=DEV)
+    out = bl.bitlinear_attention_decode(g_qkv, g_kc, g_vc, g_pos, H, KVH, workspace=ws).cpu().numpy()
+    ref, okc, ovc = oracle.attention_decode(qkv, kc, vc, pos, H, KVH, 10000.0)
+    assert np.isfinite(out).all()
+    assert (np.abs(out - ref) <= attention_bound(qkv, okc, ovc, pos, H, KVH)).all()
 
 
 @pytest.mark.parametrize("M,H,KVH,C,pos", [(1, 20, 5, 4096, [4095]), (2, 64, 8, 4096, [4000, 1234]),
