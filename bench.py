@@ -310,17 +310,20 @@ def summarize_trace(trace_csv, stats_csv, out, command="--steps 80 --warmup 8 --
             if "bl::" not in name:
                 continue
             short = name.replace("void ", "").split("(")[0]
-            key = (short, int(r.get("Grid_Size_X", r.get("Grid_Size", 0))) // 256, int(r.get("Grid_Size_Y", 1)),
+            wg = int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", 256)) or 256)
+            key = (short, int(r.get("Grid_Size_X", r.get("Grid_Size", 0))) // wg, int(r.get("Grid_Size_Y", 1)),
                    r.get("VGPR_Count", r.get("Arch_VGPR_Count", "")), r.get("LDS_Block_Size", r.get("LDS_Size", "")))
             rows.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     with open(out, "w") as f:
         f.write("# rocprofv3 kernel trace of bench.py (library kernels; durations End - Start per dispatch, us)\n")
         f.write("# command (GPU box, repository root in $R):\n")
-        f.write("#   cd /tmp && rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof_bench -o trace "
-                "--output-format csv -- python3 $R/bench.py %s\n" % command)
+        outdir = os.path.basename(os.path.dirname(os.path.abspath(trace_csv))) or "prof_bench"
+        f.write("#   cd /tmp && rocprofv3 --kernel-trace --stats -d $R/gpurun_out/%s -o trace "
+                "--output-format csv -- python3 $R/bench.py %s\n" % (outdir, command))
         f.write("#   python3 bench.py --summarize-trace <trace_kernel_trace.csv> <trace_kernel_stats.csv> <this file>%s\n"
                 % ("" if command.startswith("--steps 80") else " --trace-command=%s" % command))
-        f.write("# WGs = grid X / 256 (work-groups per launch row), gridY = grid Y (token tiles; attention: head groups)\n#\n")
+        f.write("# WGs = grid X / work-group size X (work-groups per launch row), gridY = grid Y (token tiles; "
+                "attention: head groups)\n#\n")
         f.write("# %-48s %5s %5s %5s %6s %6s %8s %8s %8s\n" % ("kernel", "WGs", "gridY", "VGPR", "LDS", "calls", "avg_us",
                                                             "med_us", "min_us"))
         for key in sorted(rows):

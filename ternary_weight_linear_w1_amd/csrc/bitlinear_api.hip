@@ -120,6 +120,36 @@ void launch_k64(const bl::FwdArgs& a, int wg_per_cu, hipStream_t stream)
         hipLaunchKernelGGL((bl::gemv_k64_kernel<L, MT, CPL, R, FUSED, false, S>), dim3(gx, gy), dim3(256), lds, stream, a);
 }
 
+// One token with a fused input: the two-role kernel, 512-thread blocks, two weight
+// buffers per wave (measured on MI355X on the 100B down projection, L = 64 with 7 chunks
+// per lane: 14.8-15.2 us against 19.1-19.6 us for the 256-thread kernel with three passes
+// in flight; three buffers, a 5:3 or 7:1 split of the passes, or requesting weights before
+// the prologue's statistics were all slower).
+template <int L, int CPL>
+void launch_split(const bl::FwdArgs& a, hipStream_t stream, int wg_per_cu = 1)
+{
+    constexpr int S = 2;
+    const int64_t passes = (a.N + 256 / L - 1) / (256 / L);
+    const int64_t max_x = int64_t(cu_count()) * wg_per_cu;
+    const int gx = (int)(passes < max_x ? passes : max_x);
+    const size_t lds = (size_t)a.K;
+    const bool norm = a.gain != nullptr;
+#define BL_SPLIT(R, A, NM) \
+    hipLaunchKernelGGL((bl::gemv_split_kernel<L, CPL, S, R, A, NM>), dim3((unsigned)gx), dim3(512), lds, stream, a)
+#define BL_SPLIT_MODE(R)                                                   \
+    do {                                                                   \
+        if (a.act == 0) { if (norm) BL_SPLIT(R, 0, true); else BL_SPLIT(R, 0, false); } \
+        else if (a.act == 1) { if (norm) BL_SPLIT(R, 1, true); else BL_SPLIT(R, 1, false); } \
+        else { if (norm) BL_SPLIT(R, 2, true); else BL_SPLIT(R, 2, false); } \
+    } while (0)
+    if (a.residual)
+        BL_SPLIT_MODE(true);
+    else
+        BL_SPLIT_MODE(false);
+#undef BL_SPLIT_MODE
+#undef BL_SPLIT
+}
+
 // One token per tile: up to 4 chunks (256 codes) per lane (7 for the longest rows).
 // Launch shapes (lanes per row L, chunks per lane, rows per lane, passes in flight S,
 // blocks per CU) from graph-timed sweeps on MI355X over the BitNet 2B and 100B shapes;
@@ -156,7 +186,12 @@ bool dispatch_mt1(const bl::FwdArgs& a, hipStream_t stream)
             else
                 launch_k64<64, 1, 2, 1, FUSED, 3>(a, 3, stream);
         } else if constexpr (FUSED) {   // two blocks per CU from ~20 MB of packed weights (100B QKV, up)
-            launch_k64<32, 1, 4, 1, FUSED>(a, 2, stream);
+            // one token on >= 32 MB of packed weights (100B up): the two-role kernel, two
+            // blocks per CU (12.65 -> 11.9 us; on the 100B QKV and O it lost 0.1-0.4 us)
+            if (a.M == 1 && nk >= (int64_t(128) << 20))
+                launch_split<32, 4>(a, stream, 2);
+            else
+                launch_k64<32, 1, 4, 1, FUSED>(a, 2, stream);
         } else {   // one row per lane and more blocks keep the HBM queue fuller on long matrices
             launch_k64<32, 1, 4, 1, FUSED>(a, nk >= (int64_t(128) << 20) ? 3 : 2, stream);
         }
@@ -168,10 +203,14 @@ bool dispatch_mt1(const bl::FwdArgs& a, hipStream_t stream)
     }
     if (KC <= 512) {
         if (KC <= 448) {   // one wave per row (no cross-wave sum), 7 chunks per lane: 100B down
-            if constexpr (FUSED)
-                launch_k64<64, 1, 7, 1, FUSED, 3>(a, 1, stream);
-            else
+            if constexpr (FUSED) {
+                if (a.M == 1)
+                    launch_split<64, 7>(a, stream);   // 100B down fused: 19.1 -> 15.0 us
+                else
+                    launch_k64<64, 1, 7, 1, FUSED, 3>(a, 1, stream);
+            } else {
                 launch_k64<64, 1, 7, 1, FUSED>(a, 1, stream);
+            }
         } else if constexpr (FUSED) {
             launch_k64<128, 1, 4, 1, FUSED>(a, 1, stream);
         } else {

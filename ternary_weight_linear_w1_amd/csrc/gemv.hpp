@@ -727,6 +727,151 @@ __global__ __launch_bounds__(256) void gemv_k64_kernel(FwdArgs a)
     } while (tile < ntiles);
 }
 
+// One token, fused input, rows of L * CPL chunks (the 100B down projection: L = 64,
+// CPL = 7; the K = 8192 matrices: L = 32, CPL = 4): 512 threads in two roles. A wave's loads complete in order, so in the 256-thread kernel
+// the prologue's row loads wait behind the weight passes requested before them. Here
+// waves 0-3 run the fused prologue exactly as that kernel does (the same canonical threads
+// and order, so the same codes, scale and outputs) with no weight loads of their own in
+// flight, while waves 4-7 request their first S passes once the prologue's statistics are
+// in (requesting them at the start slows the prologue's row loads, which share the CU's
+// memory pipeline, by more than it gains) and meet the prologue at its two barriers.
+// Block b owns passes p = 0, 1, ... of RG = 256 / L rows each (rows b*RG + p*stride ..;
+// within each role, lanes of group (tid mod 256) / L share a row); of its n passes the
+// streaming waves compute the first n - n/4 and the prologue waves the rest, each wave
+// with S weight buffers in turn.
+template <int L, int CPL, int S, bool RES, int ACT, bool NORM>
+__global__ __launch_bounds__(512) void gemv_split_kernel(FwdArgs a)
+{
+    constexpr int NT = 256, RG = NT / L;
+    static_assert(L == 32 || L == 64, "a row within one wave");
+    constexpr int UP = preloaded_units<L, 1, CPL, 1>();
+    constexpr int NK = kept_units<L, 1, CPL, 1>();
+    using MD = Mode<ACT, NORM>;
+    extern __shared__ uint4 lds_codes[];
+    __shared__ int csum[1][4];
+    __shared__ float s_tok;
+    // the wave index through readfirstlane: the compiler then knows the pass ranges below
+    // are wave-uniform and keeps the weight descriptors in scalar registers
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), j = tid % L;
+    const int slot = (tid % NT) / L;
+    const bool pro = wave < 4;
+    const int KC = a.K >> 6, KB = a.K >> 2;
+    const int64_t N = a.N;
+    const int64_t pstride = (int64_t)gridDim.x * RG;
+    const int64_t rb0 = (int64_t)blockIdx.x * RG;
+    const int n = rb0 < N ? (int)((N - rb0 + pstride - 1) / pstride) : 0;   // this block's passes
+    const int ps = n - n / 4;                                               // streaming waves' share
+
+    int woff[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = j + i * L;
+        woff[i] = c < KC ? slot * KB + c * 16 : kOob;
+    }
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc((void*)a.Y, (short)0, (int)(N * 4), kBufFlags);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        a.acc ? (void*)a.acc : (void*)a.Y, (short)0, a.acc ? (int)(N * 4) : 0, kBufFlags);
+    // pass p of this block, or nothing (a zero-size range: loads give 0, stores drop) when
+    // p lies outside [p0, p1); the loads are unconditional so that no branch surrounds them
+    auto load_pass = [&](int p, int p0, int p1, u32x4 (&w)[CPL], float& yo) {
+        const int64_t rb = p >= p0 && p < p1 ? rb0 + p * pstride : N;
+        if constexpr (RES) {
+            const int64_t row = rb + slot;
+            yo = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(ry, j == 0 && row < N ? (int)(row * 4) : kOob, 0, 0));
+        }
+        const int64_t rows = rb < N ? ((N - rb) < RG ? (N - rb) : RG) : 0;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (rb < N ? rb : 0) * KB), (short)0, (int)(rows * KB), kBufFlags);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, woff[i], 0, 2));
+    };
+
+    UnitRaw pu[UP];
+    if (pro) {
+        const RowRes rr = row_res(a.X, 0, a.K, ACT, a.gain);
+#pragma unroll
+        for (int i = 0; i < UP; ++i)
+            unit_load_xy(rr, tid + NT * i, MD::kY, pu[i]);
+    }
+    const float gamma = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(
+                   __builtin_amdgcn_make_buffer_rsrc((void*)a.gamma, (short)0, 4, kBufFlags), 0, 0, 0));
+    u32x4 wbuf[S][CPL];
+    float ybuf[S];
+    if (pro) {
+        float s[1];
+        fused_stage<1, UP, NK, 0, MD>(a, 0, 1, lds_codes, s, csum, pu);
+        if (tid == 0)
+            s_tok = s[0];
+    } else {
+        __syncthreads();   // the prologue's statistics barrier
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            load_pass(i, 0, ps, wbuf[i], ybuf[i]);
+    }
+    __syncthreads();       // codes, code sums and the token scale are in LDS
+    const int p0 = pro ? ps : 0, p1 = pro ? n : ps;
+    if (pro) {
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            load_pass(p0 + i, p0, p1, wbuf[i], ybuf[i]);
+    }
+
+    uint32_t act[CPL][16];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = j + i * L;
+        const int cc = c < KC ? c : KC - 1;   // chunks past the row meet zero weights
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint4 v = lds_codes[4 * cc + d];
+            act[i][4 * d + 0] = v.x;
+            act[i][4 * d + 1] = v.y;
+            act[i][4 * d + 2] = v.z;
+            act[i][4 * d + 3] = v.w;
+        }
+    }
+    const int32_t xs = j == 0 ? (csum[0][0] + csum[0][1]) + (csum[0][2] + csum[0][3]) : 0;
+    const float csc = gamma / s_tok;
+
+    // the same arithmetic as the 256-thread kernel's pass (fields masked in place, one
+    // accumulator per field)
+    auto compute_pass = [&](int p, const u32x4 (&w)[CPL], float yo) {
+        int32_t part[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t u[4] = {wd[d] & 0x03030303u, wd[d] & 0x0C0C0C0Cu, wd[d] & 0x30303030u,
+                                       (wd[d] >> 2) & 0x30303030u};
+#pragma unroll
+                for (int f = 0; f < 4; ++f)
+                    part[f] = __builtin_amdgcn_sdot4((int)u[f], (int)act[i][4 * d + f], part[f], false);
+            }
+        }
+        const int32_t sum = part[0] + (part[1] >> 2) + ((part[2] + part[3]) >> 4);
+        const int32_t accv = group_sum<L>(sum - xs);
+        const int64_t row = rb0 + p * pstride + slot;
+        const int off = j == 0 && row < N ? (int)(row * 4) : kOob;
+        float yv = (float)accv * csc;
+        if constexpr (RES)
+            yv = yo + yv;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, yv), ry, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(accv, ra, off, 0, 0);
+    };
+    for (int p = p0; p < p1; p += S) {
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            if (p + i < p1)
+                compute_pass(p + i, wbuf[i], ybuf[i]);
+            load_pass(p + i + S, p0, p1, wbuf[i], ybuf[i]);
+        }
+    }
+}
+
 // Any K % 4 == 0 and any alignment of the packed rows: byte loads, one wave per row,
 // four tokens per tile. Used for shapes the 16-byte chunked kernel does not cover.
 template <bool FUSED>

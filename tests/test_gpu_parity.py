@@ -196,6 +196,14 @@ FWD_CASES = [
     # pre-quantized rows of 257..448 chunks (one wave per row, 7 chunks per lane, some lanes
     # holding fewer) and of 449..512 (four waves per row)
     (1, 77, 20480, None), (1, 45, 16448, None), (1, 9, 28672, None), (1, 21, 30720, None),
+    # fused rows of 257..448 chunks at one token: the two-role kernel (waves 0-3 derive the
+    # codes, waves 4-7 stream weights); one pass per block, a ragged last pass, 8-9 passes
+    # (6-7 streamed, 2 by the prologue waves) and 13 (10 and 3: an odd count in turns of two)
+    (1, 1, 28672, None), (1, 5, 20480, "norm"), (1, 1030, 24576, "relu2"), (1, 8200, 16448, "gated"),
+    (1, 12300, 16448, "relu2norm"), (1, 4101, 28672, "gatednorm"),
+    # the two-role kernel with 32 lanes per row (K <= 8192 on >= 128M weights, two blocks
+    # per CU): 8 rows per pass, 8-9 passes per block
+    (1, 16400, 8192, "norm"), (1, 17000, 7936, "gatednorm"),
 ]
 
 
@@ -364,6 +372,9 @@ RESIDUAL_CASES = [
     # one-token launch shapes of the decode stack and the 100B slice: two rows per lane
     # (2B up), three passes in flight (100B O: both the fused and the pre-quantized shape)
     (1, 6912, 2560, None), (1, 8192, 8192, "norm"),
+    # the two-role kernel (fused rows of 257..448 chunks, one token; 32 lanes per row on
+    # >= 128M weights)
+    (1, 300, 28672, "relu2norm"), (1, 9000, 20480, "gatednorm"), (1, 16400, 8192, "relu2"),
 ]
 
 
