@@ -778,6 +778,7 @@ def run_peaks(torch, dev):
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     P.bl_peak_stream_read.argtypes = [vp, i64, ci, ci, vp, vp]
     P.bl_peak_mfma_i8.argtypes = [ci, ci, vp, vp]
+    P.bl_peak_empty.argtypes = [ci, vp, vp]
     out = {}
     sink = torch.zeros((4096 * 256,), dtype=torch.int32, device=dev)
 
@@ -804,6 +805,12 @@ def run_peaks(torch, dev):
         del buf
         torch.cuda.empty_cache()
     out["stream_read (per launch, back to back)"] = reads
+    # the floor of a kernel boundary: launches with no work, back to back in a graph
+    empty = {}
+    for blocks in (256, 1024):
+        t = time_kernel(torch, lambda c, b=blocks: P.bl_peak_empty(b, ctypes.c_void_p(sink.data_ptr()), cur()), 2, 200)
+        empty["%d blocks" % blocks] = round(t * 1e6, 2)
+    out["empty_launch_us (graph, back to back)"] = empty
     blocks, iters = 2 * 256, 4000
     t = time_kernel(torch, lambda c: P.bl_peak_mfma_i8(iters, blocks, ctypes.c_void_p(sink.data_ptr()), cur()), 1, 5)
     ops = blocks * 4 * iters * 4 * 65536.0

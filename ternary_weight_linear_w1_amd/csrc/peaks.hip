@@ -1,6 +1,6 @@
 // peaks.hip -- calibration kernels for the measurement: the streaming-read rate a launch of
-// a given size reaches on this GPU, and the int8 matrix-core rate of a pure instruction
-// loop. Built into libbitlinear_peaks.so beside the library; only the benchmark loads it.
+// a given size reaches on this GPU, the int8 matrix-core rate of a pure instruction loop,
+// and the cost of a kernel boundary (a launch with no work). Built into libbitlinear_peaks.so beside the library; only the benchmark loads it.
 // Not part of the BitLinear path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,6 +52,14 @@ __global__ __launch_bounds__(256) void mfma_i8_kernel(int iters, int32_t* __rest
     sink[blockIdx.x * 256 + threadIdx.x] = c0[0] + c1[5] + c2[10] + c3[15];
 }
 
+// A launch with no work (its one store needs threadIdx.x == never, and never is -1): the
+// time per launch of a graph of them is what every kernel boundary costs.
+__global__ __launch_bounds__(256) void empty_kernel(int never, uint32_t* __restrict__ sink)
+{
+    if ((int)threadIdx.x == never)
+        sink[blockIdx.x] = 0u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +92,15 @@ int bl_peak_mfma_i8(int iters, int blocks, int32_t* sink, hipStream_t stream)
     if (!sink || iters <= 0 || blocks <= 0)
         return 1;
     hipLaunchKernelGGL(mfma_i8_kernel, dim3(blocks), dim3(256), 0, stream, iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// `blocks` 256-thread blocks of the empty kernel; `sink` holds `blocks` uint32 (never written).
+int bl_peak_empty(int blocks, uint32_t* sink, hipStream_t stream)
+{
+    if (!sink || blocks <= 0)
+        return 1;
+    hipLaunchKernelGGL(empty_kernel, dim3(blocks), dim3(256), 0, stream, -1, sink);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
