@@ -1014,9 +1014,10 @@ def summarize_mfma(counter_csv, out):
     vals = {}
     with open(counter_csv) as f:
         for r in csv.DictReader(f):
-            if "gemm_mfma" not in r["Kernel_Name"]:
+            if "bl::gemm_" not in r["Kernel_Name"] or "reduce" in r["Kernel_Name"]:
                 continue
-            key = (r["Kernel_Name"].replace("void ", "").split("(")[0], int(r["Grid_Size"]) // 256)
+            wg = int(r.get("Workgroup_Size", 256) or 256)
+            key = (r["Kernel_Name"].replace("void ", "").split("(")[0], int(r["Grid_Size"]) // wg)
             d = vals.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), {})
             d[r["Counter_Name"]] = float(r["Counter_Value"])
     with open(out, "w") as f:

@@ -257,6 +257,38 @@ GEMM_CASES = [
 ]
 
 
+# Many tiles of 64 x 256 (at least 40% of a round of two blocks on each of 256 CUs): the
+# two-role kernel (activation loader waves). Ragged M and N, K tails of 64, a single K step.
+ROLES_CASES = [(1216, 2600, 2624), (1000, 6912, 192), (2048, 2560, 64), (1280, 3840, 6912)]
+
+
+@pytest.mark.parametrize("M,N,K", ROLES_CASES)
+def test_gemm_roles_parity(M, N, K):
+    """Codes, accumulators and outputs bit-exact against the oracle on sampled output
+    columns (every row), with and without the int32 copy, and the residual form equal to
+    the plain output added in fp32."""
+    w = latents(N, K, 7100 + N + K)
+    x = make_acts(M, K, 8100 + M + K, heavy=True)
+    print("roles GEMM case M=%d N=%d K=%d" % (M, N, K), flush=True)
+    packed, gamma = bl.bitlinear_pack_weights(up(w))
+    xq, s = bl.bitlinear_quantize_act(up(x))
+    y, acc = bl.bitlinear_forward(xq, s, packed, gamma, acc=True)
+    y_plain = bl.bitlinear_forward(xq, s, packed, gamma)
+    y0 = datagen.outlier_acts(M, N, 8200 + M + N)
+    yr = up(y0)
+    bl.bitlinear_forward(xq, s, packed, gamma, y=yr, residual=True)
+    rng = np.random.default_rng(N + K)
+    cols = np.unique(np.concatenate([rng.choice(N, size=40, replace=False), [0, 255, 256, N - 1]]))
+    opacked, ogamma, _ = oracle.pack_weights(w)
+    oxq, os_ = oracle.quantize_act(x)
+    assert np.array_equal(down(xq), oxq)
+    oacc, oy = oracle.forward(oxq, os_, oracle.weight_codes(w[cols], ogamma), ogamma)
+    assert np.array_equal(down(acc)[:, cols], oacc)
+    assert np.array_equal(down(y)[:, cols].view(np.int32), oy.view(np.int32))
+    assert np.array_equal(down(y_plain).view(np.int32), down(y).view(np.int32))
+    assert np.array_equal(down(yr).view(np.int32), oracle_residual(y0, down(y)).view(np.int32))
+
+
 @pytest.mark.parametrize("M,N,K", GEMM_CASES)
 def test_gemm_parity(M, N, K):
     """Codes, accumulators and outputs bit-exact against the oracle; the call without the
