@@ -1010,20 +1010,17 @@ int bitlinear_attention_decode(const float* qkv, uint16_t* k_cache, uint16_t* v_
     float* part_acc = static_cast<float*>(workspace);
     float* part_ml = part_acc + M * heads * S * bl::kAttnD;
     // One 64-position sub-chunk per block while that needs at most two blocks per compute
-    // unit. Else each block walks several sub-chunks (at most 4 query heads per block, which
-    // keeps the running state in registers) so that about three blocks per compute unit
-    // remain: measured on MI355X at 32768 positions, 30.7 us against 32.4 at four blocks
-    // per unit, 34 at two and 34.7 at six.
+    // unit and a block holds at most 4 query heads. Else each block walks several
+    // sub-chunks (at most 4 query heads per block, which keeps the running state in
+    // registers) so that about three blocks per compute unit remain: measured on MI355X at
+    // 32768 positions, 30.7 us against 32.4 at four blocks per unit, 34 at two and 34.7 at
+    // six; with 8 query heads per KV head (100B, 4096 positions) 15.4 us against 17.3 for one
+    // sub-chunk and 8 heads per block.
     const int64_t G = heads / kv_heads;
     const int64_t cus = cu_count();
-    const int GB1 = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
-    const bool loop = S * kv_heads * (G / GB1) * M > 2 * cus;
-    int GB = GB1;
-    int64_t cpb = 1;
-    if (loop) {
-        GB = GB1 > 4 ? 4 : GB1;
-        cpb = (S * kv_heads * (G / GB) * M + 3 * cus - 1) / (3 * cus);
-    }
+    const int GB = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;   // query heads per block
+    const bool loop = S * kv_heads * (G / GB) * M > 2 * cus || G % 8 == 0;
+    const int64_t cpb = loop ? (S * kv_heads * (G / GB) * M + 3 * cus - 1) / (3 * cus) : 1;
     if (kv_heads * (G / GB) > 65535)
         return BITLINEAR_ERR_SHAPE;
     bl::AttnArgs a{qkv, k_cache, v_cache, pos, out, part_acc, part_ml, (int)heads, (int)kv_heads, (int)capacity,
@@ -1036,7 +1033,6 @@ int bitlinear_attention_decode(const float* qkv, uint16_t* k_cache, uint16_t* v_
         }
     } else {
         switch (GB) {
-        case 8: launch_attn<8, false>(a, (int)M, stream); break;
         case 4: launch_attn<4, false>(a, (int)M, stream); break;
         case 2: launch_attn<2, false>(a, (int)M, stream); break;
         default: launch_attn<1, false>(a, (int)M, stream); break;
