@@ -287,6 +287,16 @@ def test_gemm_roles_parity(M, N, K):
     assert np.array_equal(down(y)[:, cols].view(np.int32), oy.view(np.int32))
     assert np.array_equal(down(y_plain).view(np.int32), down(y).view(np.int32))
     assert np.array_equal(down(yr).view(np.int32), oracle_residual(y0, down(y)).view(np.int32))
+    # the fused call (quantize into a workspace, then this product) gives the same bits,
+    # plain and with a gated subln input
+    assert np.array_equal(down(bl.bitlinear_forward_f32(up(x), packed, gamma)).view(np.int32),
+                          down(y).view(np.int32))
+    xg = make_acts(M, 2 * K, 8300 + M + K)
+    gain, act = pro_args("gatednorm", K, 8400 + K)
+    xqg, sg = bl.bitlinear_quantize_act(up(xg), up(gain), EPS, act)
+    yg = bl.bitlinear_forward(xqg, sg, packed, gamma)
+    ygf = bl.bitlinear_forward_f32(up(xg), packed, gamma, up(gain), EPS, act)
+    assert np.array_equal(down(ygf).view(np.int32), down(yg).view(np.int32))
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES)
