@@ -65,6 +65,7 @@ PAIRS = [
     ((12, 8192, 28672, "plain", 0), (10, 4096, 16384, "norm", 0)),        # K split: partials in the scratch
     ((256, 3840, 2560, "norm", 1), (17, 1024, 2560, "gated", 1)),          # residual forms
     ((2048, 2560, 6912, "relu2norm", 0), (1, 6912, 2560, "plain", 0)),     # 14 MB of codes; one token: no scratch
+    ((16, 4096, 28672, "relu2norm", 0), (1, 8192, 28672, "relu2norm", 1)),  # one token, long rows: two-role kernel
 ]
 
 
