@@ -779,6 +779,7 @@ def run_peaks(torch, dev):
     P.bl_peak_stream_read.argtypes = [vp, i64, ci, ci, vp, vp]
     P.bl_peak_mfma_i8.argtypes = [ci, ci, vp, vp]
     P.bl_peak_empty.argtypes = [ci, vp, vp]
+    P.bl_peak_mfma_valu.argtypes = [ci, ci, ci, vp, vp]
     out = {}
     sink = torch.zeros((4096 * 256,), dtype=torch.int32, device=dev)
 
@@ -816,6 +817,15 @@ def run_peaks(torch, dev):
     ops = blocks * 4 * iters * 4 * 65536.0
     out["mfma_i8_loop"] = {"POPS": round(ops / t / 1e15, 3), "frac_int8_peak": round(ops / t / 1e15 / 5.0, 4),
                            "us": round(t * 1e6, 1)}
+    # how much vector work the other wave of a SIMD can issue while the matrix core runs
+    # (one matrix-core wave and one vector wave per SIMD, one 512-thread block per CU)
+    co = {}
+    blocks, iters = 256, 4000
+    for nv in (0, 2, 4, 6, 8, 12):
+        t = time_kernel(torch, lambda c, n=nv: P.bl_peak_mfma_valu(n, iters, blocks, ctypes.c_void_p(sink.data_ptr()),
+                                                                    cur()), 1, 5)
+        co["%d valu per mfma" % nv] = round(blocks * 4 * iters * 4 * 65536.0 / t / 1e15, 3)
+    out["mfma_i8_POPS_with_valu_on_other_wave"] = co
     x = torch.ones((1 << 28,), dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
     t = time_kernel(torch, lambda c: y.copy_(x), 1, 10)

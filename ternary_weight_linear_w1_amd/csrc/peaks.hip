@@ -1,6 +1,7 @@
 // peaks.hip -- calibration kernels for the measurement: the streaming-read rate a launch of
-// a given size reaches on this GPU, the int8 matrix-core rate of a pure instruction loop,
-// and the cost of a kernel boundary (a launch with no work). Built into libbitlinear_peaks.so beside the library; only the benchmark loads it.
+// a given size reaches on this GPU, the int8 matrix-core rate of a pure instruction loop and
+// with vector-ALU work from another wave on the same SIMD, and the cost of a kernel boundary
+// (a launch with no work). Built into libbitlinear_peaks.so beside the library; only the benchmark loads it.
 // Not part of the BitLinear path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,6 +53,45 @@ __global__ __launch_bounds__(256) void mfma_i8_kernel(int iters, int32_t* __rest
     sink[blockIdx.x * 256 + threadIdx.x] = c0[0] + c1[5] + c2[10] + c3[15];
 }
 
+// Matrix-core / vector-ALU co-issue: 512-thread blocks, one per CU; waves 0-3 (one per SIMD)
+// run the four-chain MFMA loop above, waves 4-7 issue NV independent v_alignbit_b32 per MFMA
+// of their SIMD's matrix-core wave (eight register chains, no memory). The launch time
+// against NV = 0 shows how much vector work another wave can issue while the matrix core
+// runs.
+template <int NV>
+__global__ __launch_bounds__(512) void mfma_valu_kernel(int iters, int32_t* __restrict__ sink)
+{
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    int s = 0;
+    if (wave < 4) {
+        const pk_v4i a = {lane & 3, 1, (lane >> 2) & 1, 1};
+        const pk_v4i b = {1, lane & 1, 1, 0};
+        pk_v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+        for (int i = 0; i < iters; ++i) {
+            c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, b, c3, 0, 0, 0);
+        }
+        s = c0[0] + c1[5] + c2[10] + c3[15];
+    } else if (NV > 0) {
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            w[j] = 0x9e3779b9u * (j + 3) + lane;
+        for (int i = 0; i < iters; ++i) {
+#pragma unroll
+            for (int v = 0; v < 4 * NV; ++v)
+                w[v & 7] = __builtin_amdgcn_alignbit(w[v & 7], w[(v + 1) & 7], 3);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            s += (int)w[j];
+    }
+    sink[blockIdx.x * 512 + threadIdx.x] = s;
+}
+
 // A launch with no work (its one store needs threadIdx.x == never, and never is -1): the
 // time per launch of a graph of them is what every kernel boundary costs.
 __global__ __launch_bounds__(256) void empty_kernel(int never, uint32_t* __restrict__ sink)
@@ -92,6 +132,25 @@ int bl_peak_mfma_i8(int iters, int blocks, int32_t* sink, hipStream_t stream)
     if (!sink || iters <= 0 || blocks <= 0)
         return 1;
     hipLaunchKernelGGL(mfma_i8_kernel, dim3(blocks), dim3(256), 0, stream, iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// The co-issue loop on `blocks` 512-thread blocks with nv (0, 2, 4, 6, 8 or 12) vector ops
+// per MFMA on the second wave of each SIMD; `sink` holds blocks * 512 int32. Operations per
+// launch: blocks * 4 waves * iters * 4 * 65536.
+int bl_peak_mfma_valu(int nv, int iters, int blocks, int32_t* sink, hipStream_t stream)
+{
+    if (!sink || iters <= 0 || blocks <= 0)
+        return 1;
+    switch (nv) {
+    case 0: hipLaunchKernelGGL(mfma_valu_kernel<0>, dim3(blocks), dim3(512), 0, stream, iters, sink); break;
+    case 2: hipLaunchKernelGGL(mfma_valu_kernel<2>, dim3(blocks), dim3(512), 0, stream, iters, sink); break;
+    case 4: hipLaunchKernelGGL(mfma_valu_kernel<4>, dim3(blocks), dim3(512), 0, stream, iters, sink); break;
+    case 6: hipLaunchKernelGGL(mfma_valu_kernel<6>, dim3(blocks), dim3(512), 0, stream, iters, sink); break;
+    case 8: hipLaunchKernelGGL(mfma_valu_kernel<8>, dim3(blocks), dim3(512), 0, stream, iters, sink); break;
+    case 12: hipLaunchKernelGGL(mfma_valu_kernel<12>, dim3(blocks), dim3(512), 0, stream, iters, sink); break;
+    default: return 1;
+    }
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
