@@ -310,7 +310,7 @@ def test_attention_rejects_before_launch(L):
 
 
 def test_peaks_library_exports_and_rejects():
-    """The benchmark's calibration kernels: both entries exported; invalid arguments are
+    """The benchmark's calibration kernels: every entry exported; invalid arguments are
     rejected before any launch (no GPU needed)."""
     if not os.path.exists(_build.PEAKS_LIB):
         _build.build()
@@ -325,3 +325,9 @@ def test_peaks_library_exports_and_rejects():
     assert K.bl_peak_stream_read(a, 1024, 256, 3, a, None) == 1           # unroll 2, 4 or 8
     assert K.bl_peak_stream_read(a, 1024, 0, 4, a, None) == 1
     assert K.bl_peak_mfma_i8(0, 256, a, None) == 1 and K.bl_peak_mfma_i8(10, 256, None, None) == 1
+    K.bl_peak_mfma_valu.argtypes = [ci, ci, ci, vp, vp]
+    K.bl_peak_empty.argtypes = [ci, vp, vp]
+    assert K.bl_peak_mfma_valu(3, 10, 256, a, None) == 1                  # vector ops 0, 2, 4, 6, 8, 12
+    assert K.bl_peak_mfma_valu(4, 0, 256, a, None) == 1 and K.bl_peak_mfma_valu(4, 10, 0, a, None) == 1
+    assert K.bl_peak_mfma_valu(4, 10, 256, None, None) == 1
+    assert K.bl_peak_empty(0, a, None) == 1 and K.bl_peak_empty(256, None, None) == 1
