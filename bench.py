@@ -780,6 +780,7 @@ def run_peaks(torch, dev):
     P.bl_peak_mfma_i8.argtypes = [ci, ci, vp, vp]
     P.bl_peak_empty.argtypes = [ci, vp, vp]
     P.bl_peak_mfma_valu.argtypes = [ci, ci, ci, vp, vp]
+    P.bl_peak_lds_read.argtypes = [ci, ci, vp, vp]
     out = {}
     sink = torch.zeros((4096 * 256,), dtype=torch.int32, device=dev)
 
@@ -826,6 +827,13 @@ def run_peaks(torch, dev):
                                                                     cur()), 1, 5)
         co["%d valu per mfma" % nv] = round(blocks * 4 * iters * 4 * 65536.0 / t / 1e15, 3)
     out["mfma_i8_POPS_with_valu_on_other_wave"] = co
+    # LDS read rate (ds_read_b128, conflict-free, 1024-thread blocks, one and four per CU)
+    lds = {}
+    for blocks in (256, 1024):
+        t = time_kernel(torch, lambda c, b=blocks: P.bl_peak_lds_read(2000, b, ctypes.c_void_p(sink.data_ptr()), cur()),
+                        1, 5)
+        lds["%d blocks" % blocks] = round(blocks * 1024 * 2000 * 4 * 16.0 / t / 1e12, 1)
+    out["lds_read_TB/s (all CUs)"] = lds
     x = torch.ones((1 << 28,), dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
     t = time_kernel(torch, lambda c: y.copy_(x), 1, 10)

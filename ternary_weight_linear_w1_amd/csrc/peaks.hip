@@ -1,7 +1,7 @@
 // peaks.hip -- calibration kernels for the measurement: the streaming-read rate a launch of
 // a given size reaches on this GPU, the int8 matrix-core rate of a pure instruction loop and
-// with vector-ALU work from another wave on the same SIMD, and the cost of a kernel boundary
-// (a launch with no work). Built into libbitlinear_peaks.so beside the library; only the benchmark loads it.
+// with vector-ALU work from another wave on the same SIMD, the LDS read rate, and the cost of
+// a kernel boundary (a launch with no work). Built into libbitlinear_peaks.so beside the library; only the benchmark loads it.
 // Not part of the BitLinear path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -92,6 +92,33 @@ __global__ __launch_bounds__(512) void mfma_valu_kernel(int iters, int32_t* __re
     sink[blockIdx.x * 512 + threadIdx.x] = s;
 }
 
+// LDS read rate: 1024-thread blocks, every thread reading 16 bytes per ds_read_b128 at
+// lane-contiguous (conflict-free) addresses of a 64 KB block-local buffer, four reads in
+// flight, `iters` rounds; the xor of everything read is stored per thread.
+__global__ __launch_bounds__(1024) void lds_read_kernel(int iters, uint32_t* __restrict__ sink)
+{
+    constexpr int NT = 1024, U = 4;
+    __shared__ pk_u32x4 buf[NT * U];
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        buf[tid + NT * u] = pk_u32x4{(uint32_t)tid, (uint32_t)u, 3u, 5u};
+    __syncthreads();
+    pk_u32x4 acc = {0u, 0u, 0u, 0u};
+    int base = tid;
+    for (int i = 0; i < iters; ++i) {
+        pk_u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = buf[(base + NT * u) & (NT * U - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            acc ^= v[u];
+        base += 64;
+    }
+    sink[blockIdx.x * NT + tid] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 // A launch with no work (its one store needs threadIdx.x == never, and never is -1): the
 // time per launch of a graph of them is what every kernel boundary costs.
 __global__ __launch_bounds__(256) void empty_kernel(int never, uint32_t* __restrict__ sink)
@@ -151,6 +178,16 @@ int bl_peak_mfma_valu(int nv, int iters, int blocks, int32_t* sink, hipStream_t 
     case 12: hipLaunchKernelGGL(mfma_valu_kernel<12>, dim3(blocks), dim3(512), 0, stream, iters, sink); break;
     default: return 1;
     }
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// The LDS read loop on `blocks` 1024-thread blocks; `sink` holds blocks * 1024 uint32.
+// Bytes read per launch: blocks * 1024 * iters * 4 * 16.
+int bl_peak_lds_read(int iters, int blocks, uint32_t* sink, hipStream_t stream)
+{
+    if (!sink || iters <= 0 || blocks <= 0)
+        return 1;
+    hipLaunchKernelGGL(lds_read_kernel, dim3(blocks), dim3(1024), 0, stream, iters, sink);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

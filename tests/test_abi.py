@@ -331,3 +331,6 @@ def test_peaks_library_exports_and_rejects():
     assert K.bl_peak_mfma_valu(4, 0, 256, a, None) == 1 and K.bl_peak_mfma_valu(4, 10, 0, a, None) == 1
     assert K.bl_peak_mfma_valu(4, 10, 256, None, None) == 1
     assert K.bl_peak_empty(0, a, None) == 1 and K.bl_peak_empty(256, None, None) == 1
+    K.bl_peak_lds_read.argtypes = [ci, ci, vp, vp]
+    assert K.bl_peak_lds_read(0, 256, a, None) == 1 and K.bl_peak_lds_read(10, 0, a, None) == 1
+    assert K.bl_peak_lds_read(10, 256, None, None) == 1
